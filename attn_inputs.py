@@ -1,0 +1,108 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module is the only code shared by the HIP path's tests/benchmark and the
+CPU oracle: it draws inputs and describes shapes, and holds none of the
+attention arithmetic.  Inputs are drawn on the host once, rounded to the
+16-bit dtype, and the same bytes go to the GPU and (as bit patterns) to the
+oracle.
+
+Recipe: ``torch.Generator('cpu').manual_seed(seed)``; Q, K, V drawn in that
+order with ``torch.randn(..., dtype=float32)`` (iid N(0,1)); multiplied by
+``amplitude``; rounded to fp16/bf16 with ``.to(dtype)`` (round to nearest
+even).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention-forward problem: shapes, dtype, masking and input scale."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    window: int = 0
+    amplitude: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def label(self) -> str:
+        mask = "causal" if self.causal else "full"
+        if self.window:
+            mask += f"_w{self.window}"
+        return (f"{self.name}:B{self.B}_Hq{self.Hq}_Hkv{self.Hkv}_N{self.N}_d{self.d}_"
+                f"{self.dtype}_{mask}")
+
+
+def _lab(N: int, causal: bool) -> Workload:
+    return Workload("lab", 2, 4, 4, N, 64, "f16", causal,
+                    note="Lab 02 (Triton flash forward), Bloque D correctness protocol")
+
+
+# The pages' workloads (shapes from "Lab 02", "Bloque D"/"Condiciones de parada";
+# the small-model anchor L=12, h=768, d=64, N=2048 of "00 - Por que la atencion
+# domina la inferencia"; GQA/MQA and long context from the same pages).
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 12, 12, 64, 64, "f16", True,
+                     note="64-token anchor sequence, 12 heads of d=64"),
+    **{f"lab_n{N}_{'causal' if c else 'full'}": _lab(N, c)
+       for N in (256, 1000, 1024, 4096) for c in (False, True)},
+    "stress_full": Workload("stress", 1, 12, 12, 2048, 64, "f16", False, amplitude=0.5,
+                            note="small-model anchor scaled to N=2048, inputs x0.5"),
+    "stress_causal": Workload("stress", 1, 12, 12, 2048, 64, "f16", True, amplitude=0.5,
+                              note="small-model anchor scaled to N=2048, inputs x0.5"),
+    "gqa": Workload("gqa", 4, 32, 8, 8192, 128, "bf16", True,
+                    note="GQA prefill, 4 query heads per K/V head"),
+    "mqa_window": Workload("mqa", 1, 32, 1, 32768, 128, "bf16", True, window=4096,
+                           note="MQA long context, sliding window 4096"),
+    "mqa_causal": Workload("mqa", 1, 32, 1, 32768, 128, "bf16", True,
+                           note="MQA long context, full causal"),
+}
+
+
+def make_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "f16",
+             seed: int = 0, amplitude: float = 1.0):
+    """Seeded host tensors q (B,Hq,N,d), k and v (B,Hkv,N,d) in fp16/bf16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn(B, Hq, N, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, Hkv, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, Hkv, N, d, generator=g, dtype=torch.float32)
+    if amplitude != 1.0:
+        q, k, v = q * amplitude, k * amplitude, v * amplitude
+    tdt = TORCH_DTYPES[dtype]
+    return q.to(tdt).contiguous(), k.to(tdt).contiguous(), v.to(tdt).contiguous()
+
+
+def make_workload(w: Workload, seed: int = 0):
+    return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed, w.amplitude)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """The raw 16-bit patterns of a host fp16/bf16 tensor, as numpy uint16."""
+    if t.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"expected fp16/bf16, got {t.dtype}")
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def sine_matrix(rows: int, cols: int, seed: float, amplitude: float = 0.5):
+    """Deterministic input of the tiled-vs-standard demo in "Optimizaciones de
+    Atencion" (section "FlashAttention: Nunca materializar la matriz de
+    atencion"): entry (i, j) is amplitude * sin(seed + i*cols + j)."""
+    return [[math.sin(seed + i * cols + j) * amplitude for j in range(cols)]
+            for i in range(rows)]

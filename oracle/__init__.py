@@ -1,0 +1,139 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library
+never imports, links or calls it, and it shares no code with the HIP library:
+the two meet only in the seeded input generators of ``attn_inputs``.
+
+``attn_oracle.c`` is the plain definition of attention in fp64 (naive scores,
+mask, row softmax, weighted V sum, log-sum-exp), following "Lab 02 - Forward de
+flash attention en Triton", section "Bloque C", and the standard branch of the
+demo in "Optimizaciones de Atencion", section "FlashAttention: Nunca
+materializar la matriz de atencion".  ``pyref`` holds pure-Python versions for
+tiny inputs: the same definition with exactly rounded sums, and the tiled
+online-softmax recurrence of that demo, used to pin the C oracle.
+
+Parity status of every function here is listed in the module docstrings of
+``pyref`` and the tests that pin them; nothing in this package is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_attn.so")
+
+DTYPES = {"f16": 0, "bf16": 1, "f64": 2}
+
+_lib = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the C oracle with gcc (OpenMP, -O2, no fast-math)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+    lib.attn_oracle_fwd.restype = ctypes.c_int
+    lib.attn_oracle_fwd.argtypes = [vp, vp, vp, dp, dp, i64, i64, i64, i64, i64,
+                                    ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_rows.restype = ctypes.c_int
+    lib.attn_oracle_rows.argtypes = [vp, vp, vp, vp, i64, dp, dp, i64, i64, i64, i64, i64,
+                                     ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_decode.restype = ctypes.c_double
+    lib.attn_oracle_decode.argtypes = [ctypes.c_uint16, ctypes.c_int]
+    lib.attn_oracle_max_threads.restype = ctypes.c_int
+    lib.attn_oracle_max_threads.argtypes = []
+    return lib
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (building first if absent or stale) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        build(force=False)
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _as_input(x: np.ndarray, dtype: str) -> np.ndarray:
+    want = np.float64 if dtype == "f64" else np.uint16
+    if x.dtype != want:
+        raise TypeError(f"oracle input for dtype {dtype} must be {np.dtype(want).name}, got {x.dtype}")
+    return np.ascontiguousarray(x)
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D (B, H, N, d)")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    Hkv = k.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, N, d
+
+
+def oracle_fwd(q, k, v, *, scale: float, causal: bool = False, window: int = 0,
+               dtype: str = "f16", lib: ctypes.CDLL | None = None):
+    """Whole forward in fp64.  q (B,Hq,N,d), k/v (B,Hkv,N,d) as uint16 bit
+    patterns (dtype "f16"/"bf16") or float64 ("f64").  Returns (o, lse) as
+    float64 arrays of shapes (B,Hq,N,d) and (B,Hq,N)."""
+    lib = lib or load_library()
+    q, k, v = (_as_input(x, dtype) for x in (q, k, v))
+    B, Hq, Hkv, N, d = _check_shapes(q, k, v)
+    o = np.zeros((B, Hq, N, d), np.float64)
+    lse = np.zeros((B, Hq, N), np.float64)
+    rc = lib.attn_oracle_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                             o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, N, d,
+                             int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_fwd failed with code {rc}")
+    return o, lse
+
+
+def oracle_rows(q, k, v, row_ids, *, scale: float, causal: bool = False, window: int = 0,
+                dtype: str = "f16", lib: ctypes.CDLL | None = None):
+    """Selected rows in fp64.  row_ids are flat (b*Hq + h)*N + i.  Returns
+    (o (n, d), lse (n,)) as float64."""
+    lib = lib or load_library()
+    q, k, v = (_as_input(x, dtype) for x in (q, k, v))
+    B, Hq, Hkv, N, d = _check_shapes(q, k, v)
+    ids = np.ascontiguousarray(np.asarray(row_ids, dtype=np.int64))
+    n = ids.shape[0]
+    o = np.zeros((n, d), np.float64)
+    lse = np.zeros((n,), np.float64)
+    rc = lib.attn_oracle_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, ids.ctypes.data, n,
+                              o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, N, d,
+                              int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_rows failed with code {rc}")
+    return o, lse
+
+
+def decode(bits: int, dtype: str, lib: ctypes.CDLL | None = None) -> float:
+    """Exact value of one fp16/bf16 bit pattern, as the oracle decodes it."""
+    lib = lib or load_library()
+    return lib.attn_oracle_decode(int(bits) & 0xFFFF, DTYPES[dtype])
+
+
+def max_threads(lib: ctypes.CDLL | None = None) -> int:
+    lib = lib or load_library()
+    return int(lib.attn_oracle_max_threads())

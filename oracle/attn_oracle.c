@@ -1,0 +1,253 @@
+/*
+ * attn_oracle.c -- plain, slow, fp64 CPU oracle for exact scaled-dot-product
+ * attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code with the HIP library.
+ *
+ * What it computes is the plain definition of attention, written out with no
+ * tiling, no online softmax and no reordering:
+ *
+ *   for every batch b, query head h and query row i:
+ *     hk   = floor(h / (Hq / Hkv))               (contiguous GQA/MQA groups)
+ *     s_j  = scale * sum_c q[b,h,i,c] * k[b,hk,j,c]   for every visible j
+ *     m    = max_j s_j
+ *     e_j  = exp(s_j - m)
+ *     l    = sum_j e_j
+ *     o[b,h,i,c] = sum_j e_j * v[b,hk,j,c] / l
+ *     lse[b,h,i] = m + ln(l)
+ *
+ * Sources (the pages these follow):
+ *  - "Lab 02 - Forward de flash attention en Triton", section "Bloque C":
+ *    the naive reference: S = Q K^T * sm_scale, masked with -inf, row softmax,
+ *    then P V.  Section "La estructura del kernel" and "Bloque B" define the
+ *    log-sum-exp output as m + log(l) per row, with m the max of the scaled
+ *    scores.
+ *  - "Optimizaciones de Atencion" (cruxr.ai), section "FlashAttention: Nunca
+ *    materializar la matriz de atencion": the standard branch of the demo
+ *    (row max, exponentials, their sum, normalised weights, weighted V sum).
+ *  - Causal visibility j <= i: "Lab 02", "Bloque B" (mask keeps offs_m >=
+ *    offs_n) and "Errores tipicos" (a position attends to itself).
+ *  - Sliding window: "00 - Por que la atencion domina la inferencia", section
+ *    "Otras tres variantes": each token sees only its last W tokens.  Reading
+ *    taken: key j is visible from row i iff 0 <= i - j < W (W keys including
+ *    the token itself); W = 0 means no window.
+ *  - GQA/MQA: same page, same section, and "Optimizaciones de Atencion",
+ *    section "Multi-Head Latent Attention": K/V are shared by groups of query
+ *    heads.  Reading taken: contiguous groups, kv head = floor(h / G).
+ *  - A row with no visible key (unreachable through the library's argument
+ *    rules) yields o = 0 and lse = -inf, the limit of the all-masked-row guard
+ *    in "Lab 02", "Errores tipicos".
+ *
+ * Inputs are the raw bit patterns the GPU receives (fp16 or bf16), decoded
+ * exactly to double by the decoders below; a float64 input mode exists for
+ * tests that need inputs no 16-bit format can hold.  The scale is the fp32
+ * value passed to the library, widened exactly.  Scores are formed one row at
+ * a time, so memory is O(N) per thread, never O(N^2).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double decode_f16(uint16_t h)
+{
+    int sign = h >> 15;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);                 /* subnormal: frac * 2^-24 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x400), expo - 25); /* 1.frac * 2^(expo-15) */
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+static double decode_bf16(uint16_t b)
+{
+    int sign = b >> 15;
+    int expo = (b >> 7) & 0xff;
+    int frac = b & 0x7f;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -133);                /* subnormal: frac * 2^-133 */
+    else if (expo == 255)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x80), expo - 134); /* 1.frac * 2^(expo-127) */
+    return sign ? -mag : mag;
+}
+
+static double load_elem(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F16)
+        return decode_f16(((const uint16_t *)base)[idx]);
+    if (dtype == ORACLE_BF16)
+        return decode_bf16(((const uint16_t *)base)[idx]);
+    return ((const double *)base)[idx];
+}
+
+/* Exposed so the tests can pin the decoders against library conversions. */
+double attn_oracle_decode(uint16_t bits, int dtype)
+{
+    return dtype == ORACLE_F16 ? decode_f16(bits) : decode_bf16(bits);
+}
+
+int attn_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Visible key range [lo, hi] of query row i (empty when lo > hi). */
+static void visible_range(int64_t i, int64_t N, int causal, int64_t window,
+                          int64_t *lo, int64_t *hi)
+{
+    *hi = causal ? i : N - 1;
+    *lo = 0;
+    if (window > 0 && i - window + 1 > 0)
+        *lo = i - window + 1;
+}
+
+/*
+ * One output row: o_row[0..d) and *lse_out for (b, h, i).
+ * s is scratch for at least N doubles, qrow scratch for d doubles.
+ */
+static void oracle_row(const void *q, const void *k, const void *v,
+                       int64_t b, int64_t h, int64_t i,
+                       int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                       int causal, int64_t window, double scale, int dtype,
+                       double *o_row, double *lse_out, double *s, double *qrow)
+{
+    int64_t group = Hq / Hkv;
+    int64_t hk = h / group;
+    int64_t qbase = ((b * Hq + h) * N + i) * d;
+    int64_t kvhead = (b * Hkv + hk) * N * d;
+    int64_t lo, hi;
+    visible_range(i, N, causal, window, &lo, &hi);
+
+    for (int64_t c = 0; c < d; ++c) {
+        o_row[c] = 0.0;
+        qrow[c] = load_elem(q, dtype, qbase + c);
+    }
+    if (lo > hi) {
+        *lse_out = -INFINITY;
+        return;
+    }
+
+    /* scores s_j = scale * <q_i, k_j> */
+    double m = -INFINITY;
+    for (int64_t j = lo; j <= hi; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += qrow[c] * load_elem(k, dtype, kvhead + j * d + c);
+        s[j - lo] = scale * dot;
+        if (s[j - lo] > m)
+            m = s[j - lo];
+    }
+
+    /* softmax weights and the weighted sum of V rows */
+    double l = 0.0;
+    for (int64_t j = lo; j <= hi; ++j) {
+        double e = exp(s[j - lo] - m);
+        l += e;
+        for (int64_t c = 0; c < d; ++c)
+            o_row[c] += e * load_elem(v, dtype, kvhead + j * d + c);
+    }
+    for (int64_t c = 0; c < d; ++c)
+        o_row[c] /= l;
+    *lse_out = m + log(l);
+}
+
+/*
+ * Full forward.  q, o: (B, Hq, N, d); k, v: (B, Hkv, N, d); lse: (B, Hq, N);
+ * all row-major.  o and lse are float64.  Returns 0, or -1 on bad arguments,
+ * -2 when scratch cannot be allocated.
+ */
+int attn_oracle_fwd(const void *q, const void *k, const void *v,
+                    double *o, double *lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    int causal, int64_t window, float scale, int dtype)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || N < 0 || d < 1 || Hq % Hkv != 0 ||
+        window < 0 || dtype < ORACLE_F16 || dtype > ORACLE_F64)
+        return -1;
+    int64_t rows = B * Hq * N;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qrow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r) {
+                int64_t i = r % N;
+                int64_t h = (r / N) % Hq;
+                int64_t b = r / (N * Hq);
+                oracle_row(q, k, v, b, h, i, Hq, Hkv, N, d, causal, window,
+                           (double)scale, dtype, o + r * d, lse + r, s, qrow);
+            }
+        }
+        free(s);
+        free(qrow);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Selected rows only, for full-size checks where the whole output would take
+ * too long on the CPU.  row_ids[r] is the flat row index (b * Hq + h) * N + i.
+ * o: (nrows, d) float64; lse: (nrows,) float64.
+ */
+int attn_oracle_rows(const void *q, const void *k, const void *v,
+                     const int64_t *row_ids, int64_t nrows,
+                     double *o, double *lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     int causal, int64_t window, float scale, int dtype)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv != 0 ||
+        window < 0 || dtype < ORACLE_F16 || dtype > ORACLE_F64 || nrows < 0)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_ids[r] < 0 || row_ids[r] >= B * Hq * N)
+            return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qrow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t id = row_ids[r];
+                int64_t i = id % N;
+                int64_t h = (id / N) % Hq;
+                int64_t b = id / (N * Hq);
+                oracle_row(q, k, v, b, h, i, Hq, Hkv, N, d, causal, window,
+                           (double)scale, dtype, o + r * d, lse + r, s, qrow);
+            }
+        }
+        free(s);
+        free(qrow);
+    }
+    return failed ? -2 : 0;
+}

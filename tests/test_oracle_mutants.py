@@ -1,0 +1,58 @@
+"""Planted-mistake check of the oracle's pins (CPU only).
+
+Each mutant is a copy of the oracle's C source with one plausible mistake
+planted textually (a dropped term, a wrong sign, index or bound, a swapped
+operand, a wrong decoder constant).  It is compiled to a temporary library and
+the pin suite must fail on it.  The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "scale_dropped": ("s[j - lo] = scale * dot;", "s[j - lo] = dot;"),
+    "causal_excludes_self": ("*hi = causal ? i : N - 1;", "*hi = causal ? i - 1 : N - 1;"),
+    "causal_sees_next": ("*hi = causal ? i : N - 1;", "*hi = causal ? (i + 1 < N ? i + 1 : i) : N - 1;"),
+    "window_one_wider": ("*lo = i - window + 1;", "*lo = i - window;"),
+    "window_condition_off": ("if (window > 0 && i - window + 1 > 0)", "if (window > 0 && i - window > 0)"),
+    "gqa_modulo_map": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
+    "k_v_swapped": ("dot += qrow[c] * load_elem(k, dtype, kvhead + j * d + c);",
+                    "dot += qrow[c] * load_elem(v, dtype, kvhead + j * d + c);"),
+    "key_row_dropped": ("dot += qrow[c] * load_elem(k, dtype, kvhead + j * d + c);",
+                        "dot += qrow[c] * load_elem(k, dtype, kvhead + c);"),
+    "exp_sign_flipped": ("double e = exp(s[j - lo] - m);", "double e = exp(m - s[j - lo]);"),
+    "no_normalisation": ("o_row[c] /= l;", "o_row[c] /= 1.0;"),
+    "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "lse_log2": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    "value_row_wrong": ("o_row[c] += e * load_elem(v, dtype, kvhead + j * d + c);",
+                        "o_row[c] += e * load_elem(v, dtype, kvhead + lo * d + c);"),
+    "f16_bias_off": ("mag = ldexp((double)(frac | 0x400), expo - 25);",
+                     "mag = ldexp((double)(frac | 0x400), expo - 24);"),
+    "bf16_bias_off": ("mag = ldexp((double)(frac | 0x80), expo - 134);",
+                      "mag = ldexp((double)(frac | 0x80), expo - 133);"),
+    "f16_subnormal_off": ("mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
+    "max_not_tracked": ("if (s[j - lo] > m)\n            m = s[j - lo];", "if (j == lo)\n            m = s[j - lo];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    so = oracle.build(force=True, src=str(mutant_src), out=str(tmp_path / "libmutant.so"))
+    lib = oracle.load_library(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            caught.append(f"{pin.__name__}: {str(e)[:80]}")
+    assert caught, f"no pin caught mutant {name}"
