@@ -1,0 +1,32 @@
+"""Fused exact attention forward for MI355X (gfx950).
+
+A thin ctypes binding over ``lib/libattn_fwd.so``, whose C ABI is declared in
+``include/attn_fwd.h``.  The Python side only marshals arguments: every step
+of the computation runs in the HIP kernels.  PyTorch is used for device memory
+and streams.  There is no fallback: if the library is missing, every entry
+point raises.
+
+Entry points (same names as the C ABI): ``attn_fwd``, ``attn_fwd_ex``,
+``attn_fwd_validate``, ``attn_fwd_plan``, ``attn_fwd_plan_ex``,
+``attn_fwd_num_configs``, ``attn_fwd_config_desc``, ``attn_status_str``; and
+the pages' convenience form ``flash_attn_forward(q, k, v, causal=True)``
+("Lab 02 - Forward de flash attention en Triton", "Bloque A"), which also
+returns the per-row log-sum-exp.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_F16,
+    STATUS,
+    AttnError,
+    attn_fwd,
+    attn_fwd_config_desc,
+    attn_fwd_ex,
+    attn_fwd_num_configs,
+    attn_fwd_plan,
+    attn_fwd_plan_ex,
+    attn_fwd_validate,
+    attn_status_str,
+    flash_attn_forward,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,173 @@
+"""ctypes marshalling for libattn_fwd.so.  No arithmetic of the method here."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "libattn_fwd.so")
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_ARG", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_LAUNCH",
+    8: "ATTN_ERR_DEVICE",
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({attn_status_str(status)})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, f32, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    common = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cint, i64, f32, cint]
+    lib.attn_fwd.argtypes = common + [vp]
+    lib.attn_fwd.restype = cint
+    lib.attn_fwd_ex.argtypes = common + [cint, vp]
+    lib.attn_fwd_ex.restype = cint
+    lib.attn_fwd_validate.argtypes = common
+    lib.attn_fwd_validate.restype = cint
+    lib.attn_status_str.argtypes = [cint]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, i64, cint, i64, cint, i64p]
+    lib.attn_fwd_plan.restype = cint
+    lib.attn_fwd_plan_ex.argtypes = [i64, i64, i64, i64, i64, cint, i64, cint, cint, i64p]
+    lib.attn_fwd_plan_ex.restype = cint
+    lib.attn_fwd_num_configs.argtypes = []
+    lib.attn_fwd_num_configs.restype = cint
+    lib.attn_fwd_config_desc.argtypes = [cint, i64p]
+    lib.attn_fwd_config_desc.restype = cint
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int | None:
+    """Device pointer of a tensor, or an integer address, or None."""
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def attn_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype) -> int:
+    """Host-side argument checks only; returns the status code."""
+    return load_library().attn_fwd_validate(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                            B, Hq, Hkv, N, d, int(causal), window, scale, dtype)
+
+
+def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype,
+                config_id=-1, stream=None) -> None:
+    """Enqueue the forward with an explicit tile configuration; raises AttnError."""
+    rc = load_library().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                    int(causal), window, scale, dtype, config_id, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_ex")
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, stream=None) -> None:
+    """Enqueue the forward on `stream` (default: torch's current stream)."""
+    rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                 int(causal), window, scale, dtype, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd")
+
+
+def attn_fwd_plan_ex(B, Hq, Hkv, N, d, causal, window, dtype, config_id=-1) -> dict:
+    out = (ctypes.c_int64 * 7)()
+    rc = load_library().attn_fwd_plan_ex(B, Hq, Hkv, N, d, int(causal), window, dtype, config_id, out)
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_plan_ex")
+    keys = ("block_m", "block_n", "waves", "grid", "exact_tiles", "mask_mode", "config_id")
+    return dict(zip(keys, list(out)))
+
+
+def attn_fwd_plan(B, Hq, Hkv, N, d, causal, window, dtype) -> dict:
+    out = (ctypes.c_int64 * 6)()
+    rc = load_library().attn_fwd_plan(B, Hq, Hkv, N, d, int(causal), window, dtype, out)
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_plan")
+    keys = ("block_m", "block_n", "waves", "grid", "exact_tiles", "mask_mode")
+    return dict(zip(keys, list(out)))
+
+
+def attn_fwd_num_configs() -> int:
+    return int(load_library().attn_fwd_num_configs())
+
+
+def attn_fwd_config_desc(config_id: int) -> dict:
+    out = (ctypes.c_int64 * 4)()
+    rc = load_library().attn_fwd_config_desc(config_id, out)
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_config_desc")
+    return dict(zip(("query_blocks_per_wave", "waves", "block_n", "block_m"), list(out)))
+
+
+def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None,
+                       config_id: int = -1, out=None, lse=None, return_lse: bool = True):
+    """(B, Hq, N, d) query, (B, Hkv, N, d) key/value fp16 or bf16 CUDA tensors
+    -> (o, lse).  scale defaults to 1/sqrt(d).  Inputs are made contiguous."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (B, H, N, d), got shape {tuple(t.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    Hkv = k.shape[1]
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    dtype = ATTN_F16 if q.dtype == torch.float16 else ATTN_BF16
+    with torch.cuda.device(q.device):
+        attn_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, config_id,
+                    torch.cuda.current_stream(q.device).cuda_stream)
+    return out, lse

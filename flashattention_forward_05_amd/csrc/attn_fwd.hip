@@ -1,0 +1,246 @@
+// attn_fwd.hip -- C ABI of the fused attention forward (declared in
+// include/attn_fwd.h): argument checks, tile-configuration choice and launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cfloat>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_fwd.h"
+#include "attn_fwd_kernel.hpp"
+
+namespace {
+
+using attnfwd::Params;
+
+// Tile configurations compiled into the library.  qb: 32-row query blocks
+// per wave; nw: waves per workgroup; bn: keys per K/V tile.
+struct TileCfg {
+    int qb, nw, bn;
+    int bm() const { return qb * nw * 32; }
+};
+constexpr TileCfg kConfigs[] = {
+    {1, 4, 64},   // 0: 128 query rows per workgroup
+    {2, 4, 64},   // 1: 256 query rows per workgroup
+    {1, 8, 64},   // 2: 256 query rows per workgroup, 8 waves
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+// Query tiles whose first row sees fewer keys than this use the two-term P.
+constexpr int kExactBelow = 256;
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxHeads = int64_t(1) << 24;
+
+bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int mask_mode(int causal, int64_t window) {
+    if (!causal) return attnfwd::MASK_NONE;
+    return window > 0 ? attnfwd::MASK_WINDOW : attnfwd::MASK_CAUSAL;
+}
+
+int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                int64_t window, float scale, int dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (N > kMaxN || B > kMaxHeads || Hq > kMaxHeads || B * Hq > kMaxHeads) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return ATTN_ERR_ARG;
+    return ATTN_OK;
+}
+
+// Automatic choice: the larger tile when it still gives at least two
+// workgroups per compute unit, else 128-row tiles.
+int auto_config(int64_t B, int64_t Hq, int64_t N) {
+    const int64_t bh = B * Hq;
+    const int64_t wg256 = bh * ((N + 255) / 256);
+    return wg256 >= 512 ? 1 : 0;
+}
+
+template <int D, int DT, int MASK, int QB, int NW, int BN>
+hipError_t launch_one(const Params &p, int64_t grid, hipStream_t stream) {
+    Params args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_kernel<D, DT, MASK, QB, NW, BN>,
+                           dim3((unsigned)grid), dim3(NW * 64), argv, 0, stream);
+}
+
+template <int D, int DT, int MASK>
+hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
+    switch (cfg) {
+    case 0: return launch_one<D, DT, MASK, 1, 4, 64>(p, grid, stream);
+    case 1: return launch_one<D, DT, MASK, 2, 4, 64>(p, grid, stream);
+    case 2: return launch_one<D, DT, MASK, 1, 8, 64>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D, int DT>
+hipError_t launch_mask(int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream) {
+    switch (mask) {
+    case attnfwd::MASK_NONE: return launch_cfg<D, DT, attnfwd::MASK_NONE>(cfg, p, grid, stream);
+    case attnfwd::MASK_CAUSAL: return launch_cfg<D, DT, attnfwd::MASK_CAUSAL>(cfg, p, grid, stream);
+    default: return launch_cfg<D, DT, attnfwd::MASK_WINDOW>(cfg, p, grid, stream);
+    }
+}
+
+hipError_t launch(int64_t d, int dtype, int mask, int cfg, const Params &p, int64_t grid,
+                  hipStream_t stream) {
+    if (d == 64)
+        return dtype == ATTN_F16 ? launch_mask<64, 0>(mask, cfg, p, grid, stream)
+                                 : launch_mask<64, 1>(mask, cfg, p, grid, stream);
+    return dtype == ATTN_F16 ? launch_mask<128, 0>(mask, cfg, p, grid, stream)
+                             : launch_mask<128, 1>(mask, cfg, p, grid, stream);
+}
+
+// Number of query tiles (from the first) whose first row sees fewer than
+// kExactBelow keys.
+int64_t exact_tiles(int64_t N, int causal, int64_t window, int bm) {
+    const int64_t ntiles = (N + bm - 1) / bm;
+    if (!causal) return N < kExactBelow ? ntiles : 0;
+    int64_t n = 0;
+    for (int64_t t = 0; t < ntiles; ++t) {
+        int64_t vis = std::min<int64_t>(N, t * bm + 1);
+        if (window > 0) vis = std::min<int64_t>(vis, window);
+        if (vis < kExactBelow) ++n;
+    }
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_str(int status) {
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer argument";
+    case ATTN_ERR_SHAPE: return "invalid or too large shape";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype or mask";
+    case ATTN_ERR_ARG: return "scale is not finite";
+    case ATTN_ERR_ALIGN: return "pointer not aligned";
+    case ATTN_ERR_ALIAS: return "output overlaps an input or the other output";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+    }
+}
+
+int attn_fwd_validate(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                      int64_t d, int causal, int64_t window, float scale, int dtype) {
+    if (N > 0 && (!q || !k || !v || !o)) return ATTN_ERR_NULL;
+    const int rc = check_sizes(B, Hq, Hkv, N, d, causal, window, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
+    if ((mis & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_ALIGN;
+    const int64_t qbytes = B * Hq * N * d * 2;
+    const int64_t kvbytes = B * Hkv * N * d * 2;
+    const int64_t lbytes = B * Hq * N * 4;
+    if (N > 0) {
+        if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k, kvbytes) ||
+            ranges_overlap(o, qbytes, v, kvbytes))
+            return ATTN_ERR_ALIAS;
+        if (lse && (ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
+                    ranges_overlap(lse, lbytes, v, kvbytes) || ranges_overlap(lse, lbytes, o, qbytes)))
+            return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+int attn_fwd_num_configs(void) { return kNumConfigs; }
+
+int attn_fwd_config_desc(int id, int64_t *desc) {
+    if (id < 0 || id >= kNumConfigs || !desc) return ATTN_ERR_ARG;
+    desc[0] = kConfigs[id].qb;
+    desc[1] = kConfigs[id].nw;
+    desc[2] = kConfigs[id].bn;
+    desc[3] = kConfigs[id].bm();
+    return ATTN_OK;
+}
+
+int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                     int64_t window, int dtype, int config_id, int64_t *cfg) {
+    const int rc = check_sizes(B, Hq, Hkv, N, d, causal, window, 1.0f, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N);
+    const TileCfg &tc = kConfigs[id];
+    if (cfg) {
+        cfg[0] = tc.bm();
+        cfg[1] = tc.bn;
+        cfg[2] = tc.nw;
+        cfg[3] = B * Hq * ((N + tc.bm() - 1) / tc.bm());
+        cfg[4] = exact_tiles(N, causal, window, tc.bm());
+        cfg[5] = mask_mode(causal, window);
+        cfg[6] = id;
+    }
+    return ATTN_OK;
+}
+
+int attn_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                  int64_t window, int dtype, int64_t *cfg) {
+    int64_t full[7];
+    const int rc = attn_fwd_plan_ex(B, Hq, Hkv, N, d, causal, window, dtype, -1, full);
+    if (rc == ATTN_OK && cfg)
+        for (int i = 0; i < 6; ++i) cfg[i] = full[i];
+    return rc;
+}
+
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, int64_t window,
+                float scale, int dtype, int config_id, void *stream) {
+    int rc = attn_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    if (N == 0) return ATTN_OK;
+
+    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N);
+    const TileCfg &tc = kConfigs[id];
+    const int bm = tc.bm();
+    const int64_t ntiles = (N + bm - 1) / bm;
+    const int64_t grid = B * Hq * ntiles;
+    if (grid > INT_MAX) return ATTN_ERR_SHAPE;
+
+    Params p;
+    p.q = (const uint16_t *)q;
+    p.k = (const uint16_t *)k;
+    p.v = (const uint16_t *)v;
+    p.o = (uint16_t *)o;
+    p.lse = lse;
+    p.Hq = (int)Hq;
+    p.N = (int)N;
+    p.group = (int)(Hq / Hkv);
+    const int mask = mask_mode(causal, window);
+    p.window = mask == attnfwd::MASK_WINDOW ? (int)std::min<int64_t>(window, N) : 0;
+    p.n_qtiles = (int)ntiles;
+    p.n_bh = (int)(B * Hq);
+    p.exact_below = kExactBelow;
+    // fold |scale| * log2(e) into one multiplier; a negative scale flips the
+    // sign of Q instead (exact for 16-bit values).  A zero or vanishing scale
+    // is raised to 2^-100: every score then maps to an exponent that rounds
+    // to 0 in fp32, exactly what scale = 0 gives.
+    const double cabs = std::fabs((double)scale) * 1.4426950408889634;
+    p.c = (float)std::min(std::max(cabs, std::ldexp(1.0, -100)), (double)FLT_MAX);
+    p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+
+    const hipError_t err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
+    if (err == hipErrorNoBinaryForGpu || err == hipErrorInvalidDeviceFunction || err == hipErrorNoDevice ||
+        err == hipErrorInvalidDevice)
+        return ATTN_ERR_DEVICE;
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+             int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, int64_t window, float scale,
+             int dtype, void *stream) {
+    return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, -1, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) fused attention forward library
+ * (libattn_fwd.so).
+ *
+ * The operation is exact scaled-dot-product attention, forward only, with a
+ * per-row log-sum-exp output:
+ *
+ *   for every batch b, query head h and query row i (kv head hk = h / G,
+ *   G = Hq / Hkv):
+ *     s_j    = scale * sum_c q[b,h,i,c] * k[b,hk,j,c]     for visible j
+ *     o[b,h,i,:] = sum_j softmax(s)_j * v[b,hk,j,:]
+ *     lse[b,h,i] = ln sum_j exp(s_j)
+ *
+ * Sources: "Lab 02 - Forward de flash attention en Triton", sections "La
+ * estructura del kernel" (pointers, scale, log-sum-exp per row, one program per
+ * batch x head x query tile), "Bloque A" (the wrapper over (B, H, N, d) 16-bit
+ * tensors), "Bloque B" (the tiled online-softmax body, fp32 running max, sum
+ * and accumulator, causal mask that keeps key <= query), "Bloque C" (the naive
+ * definition) and "Errores tipicos" (contiguous inputs; a row attends to
+ * itself).  Sliding window and GQA/MQA: "00 - Por que la atencion domina la
+ * inferencia", section "Otras tres variantes de attention en esta fase".
+ * The tiling and online softmax are from "Optimizaciones de Atencion",
+ * section "FlashAttention: Nunca materializar la matriz de atencion": the
+ * N x N score matrix is never written to memory.
+ *
+ * Visibility: key j is visible from query row i iff
+ *   causal == 0 : always (window must then be 0);
+ *   causal != 0 : j <= i, and when window > 0 also i - j < window (the row
+ *                 sees at most `window` keys, itself included).
+ * Query head h reads K/V head floor(h / (Hq / Hkv)) (contiguous groups; MQA is
+ * Hkv = 1).
+ *
+ * Layout: all tensors row-major and contiguous.
+ *   q, o : (B, Hq,  N, d) elements of `dtype` (16-bit)
+ *   k, v : (B, Hkv, N, d) elements of `dtype`
+ *   lse  : (B, Hq,  N) float32, natural logarithm; may be NULL (not written)
+ * All pointers are device pointers (HIP device memory of the current device).
+ *
+ * Precision: scores, softmax statistics and the output accumulator are fp32;
+ * o is rounded to `dtype` to nearest-even once, at the end.
+ *
+ * Ownership: the caller allocates, owns and frees every buffer and keeps it
+ * alive until the work enqueued on `stream` has finished.  attn_fwd allocates
+ * nothing and keeps no mutable global state, so concurrent calls on distinct
+ * streams are safe; calls whose outputs overlap race.
+ *
+ * Errors: every check below happens on the host before anything is enqueued;
+ * on any error nothing is launched and o/lse are untouched.  Device faults
+ * surface at the caller's next synchronisation.  The library never
+ * synchronises.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+typedef enum {
+    ATTN_F16 = 0,   /* IEEE binary16 */
+    ATTN_BF16 = 1   /* bfloat16 */
+} attn_dtype_t;
+
+/* Return codes. */
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* q, k, v or o is NULL while N > 0 (N == 0 reads nothing) */
+    ATTN_ERR_SHAPE = 2,       /* B, Hq, Hkv < 1, N < 0, Hq % Hkv != 0, or sizes overflow */
+    ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, window < 0, window without causal */
+    ATTN_ERR_ARG = 4,         /* scale is not finite */
+    ATTN_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    ATTN_ERR_ALIAS = 6,       /* o or lse overlaps q, k, v or each other */
+    ATTN_ERR_LAUNCH = 7,      /* the kernel launch itself failed */
+    ATTN_ERR_DEVICE = 8       /* no usable gfx950 device is current */
+} attn_status_t;
+
+/*
+ * Fused attention forward.  Enqueues the work on `stream` (a hipStream_t;
+ * NULL is the null stream) and returns without waiting.  N == 0 is a valid
+ * no-op.  scale is any finite float (the usual value is 1/sqrt(d)); it may
+ * be zero or negative.  The scaled scores scale * q.k are formed in fp32 and
+ * must be finite there; results are undefined when they overflow, and for
+ * inputs holding Inf or NaN.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+             int causal, int64_t window, float scale, int dtype, void *stream);
+
+/*
+ * The host-side argument checks of attn_fwd, alone: makes no HIP call,
+ * touches no memory behind the pointers, and returns the status attn_fwd
+ * would return before launching.
+ */
+int attn_fwd_validate(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                      int64_t d, int causal, int64_t window, float scale, int dtype);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *attn_status_str(int status);
+
+/*
+ * Describes the kernel configuration attn_fwd would launch for these sizes:
+ * writes up to 6 integers to cfg (may be NULL) -- query rows per workgroup,
+ * keys per tile, waves per workgroup, workgroups in the grid, query tiles
+ * computed with the exact two-term P, and the mask mode (0 none, 1 causal,
+ * 2 causal + window) -- and returns the status of the argument checks for a
+ * call with non-NULL, aligned, disjoint pointers.
+ */
+int attn_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                  int64_t window, int dtype, int64_t *cfg);
+
+/*
+ * Tile configurations compiled into the library, for measurement: the count,
+ * and for id in [0, count) the description desc[0..3] = {32-row query blocks
+ * per wave, waves per workgroup, keys per K/V tile, query rows per
+ * workgroup}.  attn_fwd_config_desc returns ATTN_ERR_ARG for a bad id or a
+ * NULL desc.
+ */
+int attn_fwd_num_configs(void);
+int attn_fwd_config_desc(int id, int64_t *desc);
+
+/*
+ * attn_fwd_plan for a given configuration id (-1 = the automatic choice);
+ * writes 7 integers: the 6 of attn_fwd_plan followed by the id used.
+ */
+int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                     int64_t window, int dtype, int config_id, int64_t *cfg);
+
+/*
+ * attn_fwd with an explicit tile configuration (config_id in
+ * [0, attn_fwd_num_configs()), or -1 for the automatic choice that attn_fwd
+ * makes).  Same semantics, layout, ownership and errors as attn_fwd, plus
+ * ATTN_ERR_ARG for a bad config_id.  Every configuration computes the same
+ * function; they differ only in speed.
+ */
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                int causal, int64_t window, float scale, int dtype, int config_id,
+                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

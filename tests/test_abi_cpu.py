@@ -1,0 +1,103 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and its host-side argument checks return the documented codes.  No kernel is
+launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_forward_05_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path())
+    names = declared_functions()
+    assert "attn_fwd" in names and "attn_fwd_validate" in names and "attn_status_str" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_status_strings():
+    for code in range(9):
+        assert fa.attn_status_str(code) and fa.attn_status_str(code) != "unknown status"
+    assert fa.attn_status_str(99) == "unknown status"
+
+
+A = 1 << 20          # fake, aligned, disjoint addresses; nothing is dereferenced
+GOOD = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=2, Hq=4, Hkv=2, N=100, d=64,
+            causal=1, window=0, scale=0.125, dtype=0)
+
+
+def validate(**over):
+    a = dict(GOOD, **over)
+    return fa.attn_fwd_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                a["N"], a["d"], a["causal"], a["window"], a["scale"], a["dtype"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, 0),
+    ({"lse": None}, 0),
+    ({"N": 0, "q": None, "k": None, "v": None, "o": None}, 0),
+    ({"q": None}, 1), ({"k": None}, 1), ({"v": None}, 1), ({"o": None}, 1),
+    ({"B": 0}, 2), ({"Hq": 0}, 2), ({"Hkv": 0}, 2), ({"N": -1}, 2), ({"Hq": 3}, 2),
+    ({"N": (1 << 24) + 1}, 2), ({"B": 1 << 13, "Hq": 1 << 12, "Hkv": 1 << 12}, 2),
+    ({"d": 32}, 3), ({"d": 96}, 3), ({"d": 256}, 3), ({"dtype": 2}, 3), ({"dtype": -1}, 3),
+    ({"window": -1}, 3), ({"window": 16, "causal": 0}, 3),
+    ({"scale": float("inf")}, 4), ({"scale": float("nan")}, 4),
+    ({"q": A + 8}, 5), ({"o": 4 * A + 2}, 5), ({"lse": 5 * A + 2}, 5),
+    ({"o": A}, 6), ({"o": 2 * A + 64}, 6), ({"lse": 3 * A}, 6), ({"lse": 4 * A + 16}, 6),
+])
+def test_validate_codes(over, code):
+    assert validate(**over) == code
+
+
+def test_validate_accepts_edge_values():
+    assert validate(scale=0.0) == 0
+    assert validate(scale=-3.0) == 0
+    assert validate(window=1) == 0
+    assert validate(window=1 << 40) == 0
+    assert validate(Hkv=1) == 0
+    assert validate(d=128, dtype=1) == 0
+    assert validate(q=2 * A, k=2 * A, v=2 * A) == 0      # inputs may alias each other
+
+
+def test_plan_reports_tiles():
+    p = fa.attn_fwd_plan(4, 32, 8, 8192, 128, 1, 0, 1)
+    assert p["block_m"] * (8192 // p["block_m"]) == 8192
+    assert p["grid"] == 4 * 32 * (8192 // p["block_m"])
+    assert p["mask_mode"] == 1 and p["exact_tiles"] >= 1
+    assert fa.attn_fwd_plan(1, 1, 1, 100, 64, 0, 0, 0)["exact_tiles"] == 1   # short non-causal rows
+    assert fa.attn_fwd_plan(1, 1, 1, 5000, 64, 0, 0, 0)["exact_tiles"] == 0
+    assert fa.attn_fwd_plan(1, 32, 1, 32768, 128, 1, 4096, 1)["mask_mode"] == 2
+    for cid in range(fa.attn_fwd_num_configs()):
+        desc = fa.attn_fwd_config_desc(cid)
+        assert desc["block_m"] == 32 * desc["query_blocks_per_wave"] * desc["waves"]
+        pe = fa.attn_fwd_plan_ex(2, 4, 4, 1000, 64, 1, 0, 0, cid)
+        assert pe["config_id"] == cid and pe["block_m"] == desc["block_m"]
+    with pytest.raises(fa.AttnError):
+        fa.attn_fwd_config_desc(fa.attn_fwd_num_configs())
+    with pytest.raises(fa.AttnError):
+        fa.attn_fwd_plan(1, 3, 2, 10, 64, 1, 0, 0)
+
+
+def test_launch_rejects_before_touching_the_gpu():
+    # argument errors come back as exceptions without any HIP call
+    with pytest.raises(fa.AttnError) as e:
+        fa.attn_fwd_ex(None, 2 * A, 3 * A, 4 * A, None, 1, 1, 1, 8, 64, 0, 0, 0.1, 0, -1, 0)
+    assert e.value.status == 1
+    with pytest.raises(fa.AttnError) as e:
+        fa.attn_fwd_ex(A, 2 * A, 3 * A, 4 * A, None, 1, 1, 1, 8, 64, 0, 0, 0.1, 0, 99, 0)
+    assert e.value.status == 4
