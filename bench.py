@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+A step runs the whole hot path over one batch of synthetic input: every
+(N, causal) variant of the workload, each one launch of the fused kernel
+through the C ABI.  Default workload: the pages' lab check (B=2, Hq=Hkv=4,
+d=64, fp16, N in {256, 1024, 4096}, causal and not; "Lab 02 - Forward de flash
+attention en Triton", "Bloque D").
+
+Metric: attention-forward TFLOP/s with 4*B*Hq*N^2*d FLOPs per variant, halved
+when causal; a sliding window counts its visible (query, key) pairs instead.
+Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line.  Extra fields: "roofline" for the dominant kernel
+(achieved = its FLOPs per launch / its mean launch time from HIP events on the
+launch stream) and "cpu_baseline" (the fp64 oracle on a bounded sample of the
+same workload, on this host's cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}     # MI355X dense fp16/bf16 MFMA, 256 CU x 2.4 GHz x 4096
+WORKLOAD_SETS = {
+    "lab": ["lab_n256_full", "lab_n256_causal", "lab_n1024_full", "lab_n1024_causal",
+            "lab_n4096_full", "lab_n4096_causal"],
+    "tiny": ["tiny"],
+    "stress": ["stress_full", "stress_causal"],
+    "gqa": ["gqa"],
+    "mqa": ["mqa_window", "mqa_causal"],
+    "mqa_window": ["mqa_window"],
+    "lab4096": ["lab_n4096_full", "lab_n4096_causal"],
+}
+
+
+def metric_flops(B, Hq, N, d, causal, window=0) -> float:
+    """4*B*Hq*N^2*d, halved for causal; with a window, 4*B*Hq*d per visible
+    (query, key) pair."""
+    if causal and window > 0 and window < N:
+        pairs = window * (window + 1) / 2 + (N - window) * window
+        return 4.0 * B * Hq * d * pairs
+    f = 4.0 * B * Hq * N * N * d
+    return f / 2 if causal else f
+
+
+def visible_keys(i, N, causal, window):
+    hi = i if causal else N - 1
+    lo = max(0, i - window + 1) if window > 0 else 0
+    return hi - lo + 1
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flashattention_forward_05_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_label: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    ent = rec.get("kernels", {}).get(kernel_label)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(workloads, budget_s: float):
+    """The oracle, untuned, on every stride-th query row of each variant, in
+    chunks until the time budget is spent; reports the achieved rate."""
+    import numpy as np
+
+    import oracle
+    from attn_inputs import make_workload, to_bits
+
+    oracle.load_library()
+    flops = 0.0
+    elapsed = 0.0
+    rows_done = 0
+    stride = 16
+    per_variant = budget_s / len(workloads)
+    for w in workloads:
+        q, k, v = (to_bits(t) for t in make_workload(w, seed=0))
+        ids = np.arange(0, w.B * w.Hq * w.N, stride, dtype=np.int64)
+        t_var = 0.0
+        for start in range(0, len(ids), 64):
+            chunk = ids[start:start + 64]
+            t0 = time.perf_counter()
+            oracle.oracle_rows(q, k, v, chunk, scale=float(np.float32(w.scale)), causal=w.causal,
+                               window=w.window, dtype=w.dtype)
+            dt = time.perf_counter() - t0
+            t_var += dt
+            rows_done += len(chunk)
+            flops += sum(4.0 * w.d * visible_keys(int(r) % w.N, w.N, w.causal, w.window) for r in chunk)
+            if t_var > per_variant:
+                break
+        elapsed += t_var
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on every {stride}th query row of each variant "
+                   f"({rows_done} rows, {flops / 1e9:.2f} GFLOP, {elapsed:.1f} s, "
+                   f"about {per_variant:.0f} s per variant)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="lab", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--config", type=int, default=-1, help="tile configuration id (-1: automatic)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the path shards by (batch, K/V head) with no exchange, see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import flashattention_forward_05_amd as fa
+    from attn_inputs import WORKLOADS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    wls = [WORKLOADS[n] for n in WORKLOAD_SETS[args.workload]]
+
+    # inputs resident in HBM before timing
+    runs = []
+    for w in wls:
+        q, k, v = (t.to(dev) for t in make_workload(w, seed=0))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
+                                   0 if w.dtype == "f16" else 1, args.config)
+        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan,
+                         flops=metric_flops(w.B, w.Hq, w.N, w.d, w.causal, w.window)))
+
+    def launch(r):
+        # the current stream is torch's capture stream while a graph is recorded
+        w = r["w"]
+        fa.attn_fwd_ex(r["q"], r["k"], r["v"], r["o"], r["lse"], w.B, w.Hq, w.Hkv, w.N, w.d,
+                       w.causal, w.window, w.scale, 0 if w.dtype == "f16" else 1, args.config,
+                       torch.cuda.current_stream(dev).cuda_stream)
+
+    for r in runs:                       # eager warm-up (also checks every launch)
+        launch(r)
+    torch.cuda.synchronize()
+
+    # one step = every variant once, captured as a HIP graph so that the host
+    # launch cost of the small variants does not stand in for kernel time
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_graph):
+        for r in runs:
+            launch(r)
+    for _ in range(args.warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps between synchronisations
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for _ in range(args.steps):
+        step_graph.replay()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e_start.elapsed_time(e_end)
+
+    # per-kernel launch duration: R back-to-back launches of one variant in a
+    # graph, bracketed by HIP events on the launch stream
+    per_kernel_ms = []
+    for r in runs:
+        reps = max(10, min(200, int(2e-3 / max(r["flops"] / 1e15, 1e-7))))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                launch(r)
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_kernel_ms.append(a.elapsed_time(b) / reps)
+        del g
+
+    total_flops = sum(r["flops"] for r in runs)
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(range(len(runs)), key=lambda j: per_kernel_ms[j])
+    dw = runs[dom]["w"]
+    achieved = runs[dom]["flops"] / (per_kernel_ms[dom] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dw.dtype]
+    kernels = []
+    for j, r in enumerate(runs):
+        kernels.append({"variant": r["w"].label(), "ms": round(per_kernel_ms[j], 5),
+                        "tflops": round(r["flops"] / (per_kernel_ms[j] * 1e-3) / 1e12, 2),
+                        "frac_of_peak": round(r["flops"] / (per_kernel_ms[j] * 1e-3) / 1e12 / peak, 4),
+                        "plan": r["plan"]})
+
+    result = {
+        "metric": "attention fwd TFLOP/s (4*B*Hq*N^2*d, x1/2 causal) & % of MI355X MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wls[0].dtype,
+        "data": "synthetic (seeded iid N(0,1) inputs, rounded to the 16-bit dtype)",
+        "config": {
+            "workload": args.workload,
+            "variants": [w.label() for w in wls],
+            "parallelism": "single GPU",
+            "tile_config": args.config,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": dw.label(),
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_from_profiles(dw.label()),
+        },
+        "kernels": kernels,
+        "frac_of_peak_whole_step": round(value / PEAK_TFLOPS[wls[0].dtype], 4),
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 5),
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wls, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

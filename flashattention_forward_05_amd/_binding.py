@@ -57,7 +57,7 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_plan_ex.restype = cint
     lib.attn_fwd_num_configs.argtypes = []
     lib.attn_fwd_num_configs.restype = cint
-    lib.attn_fwd_config_desc.argtypes = [cint, i64p]
+    lib.attn_fwd_config_desc.argtypes = [cint, i64, i64p]
     lib.attn_fwd_config_desc.restype = cint
     _lib = lib
     return lib
@@ -130,12 +130,13 @@ def attn_fwd_num_configs() -> int:
     return int(load_library().attn_fwd_num_configs())
 
 
-def attn_fwd_config_desc(config_id: int) -> dict:
-    out = (ctypes.c_int64 * 4)()
-    rc = load_library().attn_fwd_config_desc(config_id, out)
+def attn_fwd_config_desc(config_id: int, d: int = 64) -> dict:
+    out = (ctypes.c_int64 * 6)()
+    rc = load_library().attn_fwd_config_desc(config_id, d, out)
     if rc != 0:
         raise AttnError(rc, "attn_fwd_config_desc")
-    return dict(zip(("query_blocks_per_wave", "waves", "block_n", "block_m"), list(out)))
+    keys = ("query_blocks_per_wave", "waves", "block_n", "block_m", "key_groups", "stages")
+    return dict(zip(keys, list(out)))
 
 
 def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None,

@@ -16,17 +16,29 @@ namespace {
 using attnfwd::Params;
 
 // Tile configurations compiled into the library.  qb: 32-row query blocks
-// per wave; nw: waves per workgroup; bn: keys per K/V tile.
+// per wave; nwq: query waves per workgroup; ksplit: key groups per workgroup
+// (2 = a second set of waves takes the second half of the key range, merged
+// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring.  The
+// same id may use a smaller tile for d = 128 so that LDS stays within 160 KiB.
 struct TileCfg {
-    int qb, nw, bn;
-    int bm() const { return qb * nw * 32; }
+    int qb, nwq, ksplit, bn, nstage;
+    int bm() const { return qb * nwq * 32; }
+    int waves() const { return nwq * ksplit; }
 };
-constexpr TileCfg kConfigs[] = {
-    {1, 4, 64},   // 0: 128 query rows per workgroup
-    {2, 4, 64},   // 1: 256 query rows per workgroup
-    {1, 8, 64},   // 2: 256 query rows per workgroup, 8 waves
+constexpr int kNumConfigs = 4;
+constexpr TileCfg kCfg64[kNumConfigs] = {
+    {1, 4, 1, 64, 3},   // 0: 128 rows, 4 waves
+    {1, 4, 2, 64, 3},   // 1: 128 rows, 8 waves (two key groups)
+    {1, 8, 1, 64, 3},   // 2: 256 rows, 8 waves
+    {2, 4, 1, 64, 3},   // 3: 256 rows, 4 waves with 64 rows each
 };
-constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+constexpr TileCfg kCfg128[kNumConfigs] = {
+    {1, 4, 1, 64, 3},
+    {1, 4, 2, 64, 2},
+    {1, 8, 1, 64, 3},
+    {2, 4, 1, 64, 3},
+};
+const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
 // Query tiles whose first row sees fewer keys than this use the two-term P.
 constexpr int kExactBelow = 256;
@@ -55,28 +67,32 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int ca
     return ATTN_OK;
 }
 
-// Automatic choice: the larger tile when it still gives at least two
-// workgroups per compute unit, else 128-row tiles.
-int auto_config(int64_t B, int64_t Hq, int64_t N) {
-    const int64_t bh = B * Hq;
-    const int64_t wg256 = bh * ((N + 255) / 256);
-    return wg256 >= 512 ? 1 : 0;
+// Automatic choice (measured on MI355X): d = 128 with at least two 256-row
+// workgroups per compute unit runs 8 query waves of 32 rows; everything else
+// runs 128-row workgroups with two key groups, which keeps two waves per SIMD
+// busy on small grids.
+int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d) {
+    const int64_t wg256 = B * Hq * ((N + 255) / 256);
+    if (d == 128 && wg256 >= 512) return 2;
+    return 1;
 }
 
-template <int D, int DT, int MASK, int QB, int NW, int BN>
+template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
 hipError_t launch_one(const Params &p, int64_t grid, hipStream_t stream) {
     Params args = p;
     void *argv[] = {&args};
-    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_kernel<D, DT, MASK, QB, NW, BN>,
-                           dim3((unsigned)grid), dim3(NW * 64), argv, 0, stream);
+    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_kernel<D, DT, MASK, QB, NWQ, KSPLIT, BN, NSTAGE>,
+                           dim3((unsigned)grid), dim3(NWQ * KSPLIT * 64), argv, 0, stream);
 }
 
 template <int D, int DT, int MASK>
 hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
+    constexpr bool small = D == 64;
     switch (cfg) {
-    case 0: return launch_one<D, DT, MASK, 1, 4, 64>(p, grid, stream);
-    case 1: return launch_one<D, DT, MASK, 2, 4, 64>(p, grid, stream);
-    case 2: return launch_one<D, DT, MASK, 1, 8, 64>(p, grid, stream);
+    case 0: return launch_one<D, DT, MASK, 1, 4, 1, 64, 3>(p, grid, stream);
+    case 1: return launch_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2>(p, grid, stream);
+    case 2: return launch_one<D, DT, MASK, 1, 8, 1, 64, 3>(p, grid, stream);
+    case 3: return launch_one<D, DT, MASK, 2, 4, 1, 64, 3>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -156,12 +172,15 @@ int attn_fwd_validate(const void *q, const void *k, const void *v, const void *o
 
 int attn_fwd_num_configs(void) { return kNumConfigs; }
 
-int attn_fwd_config_desc(int id, int64_t *desc) {
-    if (id < 0 || id >= kNumConfigs || !desc) return ATTN_ERR_ARG;
-    desc[0] = kConfigs[id].qb;
-    desc[1] = kConfigs[id].nw;
-    desc[2] = kConfigs[id].bn;
-    desc[3] = kConfigs[id].bm();
+int attn_fwd_config_desc(int id, int64_t d, int64_t *desc) {
+    if (id < 0 || id >= kNumConfigs || !desc || (d != 64 && d != 128)) return ATTN_ERR_ARG;
+    const TileCfg &tc = tile_cfg(d, id);
+    desc[0] = tc.qb;
+    desc[1] = tc.waves();
+    desc[2] = tc.bn;
+    desc[3] = tc.bm();
+    desc[4] = tc.ksplit;
+    desc[5] = tc.nstage;
     return ATTN_OK;
 }
 
@@ -170,12 +189,12 @@ int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
     const int rc = check_sizes(B, Hq, Hkv, N, d, causal, window, 1.0f, dtype);
     if (rc != ATTN_OK) return rc;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
-    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N);
-    const TileCfg &tc = kConfigs[id];
+    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d);
+    const TileCfg &tc = tile_cfg(d, id);
     if (cfg) {
         cfg[0] = tc.bm();
         cfg[1] = tc.bn;
-        cfg[2] = tc.nw;
+        cfg[2] = tc.waves();
         cfg[3] = B * Hq * ((N + tc.bm() - 1) / tc.bm());
         cfg[4] = exact_tiles(N, causal, window, tc.bm());
         cfg[5] = mask_mode(causal, window);
@@ -201,8 +220,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
     if (N == 0) return ATTN_OK;
 
-    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N);
-    const TileCfg &tc = kConfigs[id];
+    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d);
+    const TileCfg &tc = tile_cfg(d, id);
     const int bm = tc.bm();
     const int64_t ntiles = (N + bm - 1) / bm;
     const int64_t grid = B * Hq * ntiles;

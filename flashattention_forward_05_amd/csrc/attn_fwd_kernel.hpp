@@ -1,16 +1,19 @@
 // attn_fwd_kernel.hpp -- fused exact attention forward for gfx950 (MI355X).
 //
-// One workgroup computes one (batch, query head, query tile) of BM rows; its
-// NW waves each own QB blocks of 32 query rows.  The workgroup walks the key /
-// value tiles (BN keys each) that at least one of its rows can see, keeping a
-// running row max, running row sum and an fp32 output accumulator per row, so
-// the N x N score matrix never leaves the chip.  This is the tiled online
-// softmax of "Optimizaciones de Atencion", section "FlashAttention: Nunca
-// materializar la matriz de atencion", and the kernel body of "Lab 02 - Forward
-// de flash attention en Triton", sections "La estructura del kernel" and
-// "Bloque B" (query tile outer, key/value tiles inner, fp32 m / l / O, P cast
-// to the value dtype before the P.V product, O divided by l and LSE = m + ln l
-// at the end).
+// One workgroup computes one (batch, query head, query tile) of BM rows.  Its
+// NWQ query waves each own QB blocks of 32 query rows; with KSPLIT = 2 a
+// second set of NWQ waves owns the same rows and takes the second half of the
+// key range, and the two partial results are merged in LDS at the end (the
+// rescale-and-add of partial softmax results that "Optimizaciones de
+// Atencion", section "FlashDecoding", uses to combine key chunks).  A wave
+// walks its key/value tiles (BN keys each) keeping a running row max, running
+// row sum and an fp32 output accumulator per row, so the N x N score matrix
+// never leaves the chip.  This is the tiled online softmax of that page's
+// section "FlashAttention: Nunca materializar la matriz de atencion" and the
+// kernel body of "Lab 02 - Forward de flash attention en Triton", sections "La
+// estructura del kernel" and "Bloque B" (query tile outer, key/value tiles
+// inner, fp32 m / l / O, P cast to the value dtype before P.V, O divided by l
+// and LSE = m + ln l at the end).
 //
 // gfx950 mapping (our design, not the pages'):
 //  * Scores are formed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16
@@ -26,9 +29,13 @@
 //  * V stays row-major in LDS; ds_read_b64_tr_b16 returns, to lane j of each
 //    16-lane group, column j of the 4 x 16 block the group addressed, which
 //    is the V^T A-operand layout (8 consecutive keys of one channel per lane).
-//  * K and V tiles are brought to LDS with direct global->LDS loads
-//    (global_load_lds_dwordx4), double-buffered: tile t+1 is in flight while
-//    tile t is used.  16-byte chunks are XOR-swizzled per row so that the
+//  * K and V tiles are brought to LDS by direct global->LDS loads
+//    (global_load_lds_dwordx4) into an NSTAGE-deep ring: tiles i+1 ..
+//    i+NSTAGE-2 are in flight while tile i is used.  Each ring stage is its
+//    own LDS object and the loop is unrolled over the stages, so the compiler
+//    can tell that reads of one stage do not alias loads into another; the
+//    waits for landed tiles are explicit partial vmcnt waits followed by a
+//    bare s_barrier.  16-byte chunks are XOR-swizzled per row so that the
 //    MFMA-operand reads of 16 consecutive rows hit distinct LDS banks.
 //  * Softmax runs in base 2: c = |scale| * log2(e) is folded into one FMA per
 //    score, p = v_exp_f32(s*c - m).  The running max m is only raised when a
@@ -119,14 +126,13 @@ __device__ __forceinline__ float hi_half(uint32_t u) {
         return __uint_as_float(u & 0xffff0000u);
 }
 
-// Max of a value over lanes l and l ^ 32.
+// Max / sum of a value over lanes l and l ^ 32.
 __device__ __forceinline__ float max_halves(float x) {
     uint32_t u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Sum of a value over lanes l and l ^ 32.
 __device__ __forceinline__ float sum_halves(float x) {
     uint32_t u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -151,283 +157,450 @@ __device__ __forceinline__ int swz(int row) {
         return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-__device__ __forceinline__ void wait_vmem_all() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// s_waitcnt immediate with only the vector-memory counter constrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most `younger` tiles (of LPT loads each) of this wave are
+// still in flight.
+template <int LPT>
+__device__ __forceinline__ void wait_tiles(int younger) {
+    if (younger >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+    else if (younger == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-template <int D, int DT, int MASK, int QB, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
-    constexpr int BM = NW * QB * 32;
-    constexpr int KT = D / 16;         // 16-wide d steps of S^T = K Q^T
-    constexpr int CB = D / 32;         // 32-channel blocks of O^T
-    constexpr int KB = BN / 32;        // 32-key blocks of S^T
-    constexpr int KS = BN / 16;        // 16-key steps of O^T += V^T P^T
-    constexpr int ROWB = D * 2;        // bytes per K/V row
-    constexpr int TILEB = BN * ROWB;   // bytes per K or V tile
-    constexpr int CHUNKS_PER_ROW = D / 8;
-    constexpr int LOADS = (BN * CHUNKS_PER_ROW) / (64 * NW);   // 16-B loads per lane per tensor
-    static_assert((BN * CHUNKS_PER_ROW) % (64 * NW) == 0, "tile must split evenly over the waves");
+template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
+struct Kernel {
+    static constexpr int BM = NWQ * QB * 32;
+    static constexpr int NWAVES = NWQ * KSPLIT;
+    static constexpr int KT = D / 16;          // 16-wide d steps of S^T = K Q^T
+    static constexpr int CB = D / 32;          // 32-channel blocks of O^T
+    static constexpr int KB = BN / 32;         // 32-key blocks of S^T
+    static constexpr int KS = BN / 16;         // 16-key steps of O^T += V^T P^T
+    static constexpr int ROWB = D * 2;         // bytes per K/V row
+    static constexpr int TILEB = BN * ROWB;    // bytes per K or V tile
+    static constexpr int CHUNKS_PER_ROW = D / 8;
+    static constexpr int LOADS = (BN * CHUNKS_PER_ROW) / (64 * NWQ);   // 16-B loads per lane per tensor
+    static constexpr int LPT = 2 * LOADS;                              // loads per lane per tile
+    static constexpr int STAGEB = KSPLIT * TILEB;                      // one stage of K (or V), all groups
+    static_assert((BN * CHUNKS_PER_ROW) % (64 * NWQ) == 0, "tile must split evenly over the waves");
     static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4 && (KSPLIT == 1 || KSPLIT == 2), "unsupported pipeline");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILEB];   // [stage][K or V]
+    // per-wave state
+    struct State {
+        u32x4 qf[QB][KT];
+        f32x16 oacc[QB][CB];
+        float mrun[QB];
+        float lsum[QB];
+    };
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = lane >> 5;
-    const int l32 = lane & 31;
-    const int N = p.N;
+    struct Ctx {
+        const uint16_t *kp, *vp;
+        int N, window, lane, g, l32, wave_q, kgroup;
+        int qw0, w_last;
+        float c;
+        char *kst[NSTAGE];
+        char *vst[NSTAGE];
+    };
 
-    // ---- which (batch*head, query tile) this workgroup owns; for masked
-    // runs the heaviest query tiles (most visible keys) are dispatched first.
-    const int bid = blockIdx.x;
-    const int bh = bid % p.n_bh;
-    const int rank = bid / p.n_bh;
-    const int qt = (MASK == MASK_NONE) ? rank : (p.n_qtiles - 1 - rank);
-    const int b = bh / p.Hq;
-    const int h = bh - b * p.Hq;
-    const int hkv = (p.Hq / p.group);
-    const int64_t kvhead = (int64_t)b * hkv + h / p.group;
-    const uint16_t *qp = p.q + (int64_t)bh * N * D;
-    const uint16_t *kp = p.k + kvhead * N * D;
-    const uint16_t *vp = p.v + kvhead * N * D;
-
-    const int q_tile0 = qt * BM;
-    const int qw0 = q_tile0 + wave * QB * 32;             // first row of this wave
-    const int w_last = min(qw0 + QB * 32, N) - 1;          // last valid row of this wave
-    const bool wave_live = qw0 < N;
-
-    // ---- Q fragments (MFMA B operand): lane holds row qw0 + 32*qb + l32,
-    // channels 16*kk + 8*g .. +7.  Rows past N are zero.
-    u32x4 qf[QB][KT];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = qw0 + qb * 32 + l32;
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row < N) {
-                x = *(const u32x4 *)(qp + (int64_t)row * D + kk * 16 + g * 8);
-                x ^= p.qsign;
-            }
-            qf[qb][kk] = x;
-        }
-    }
-
-    // ---- key range seen by the workgroup
-    const int q_last = min(q_tile0 + BM, N) - 1;
-    int kv_lo = 0, kv_hi = N - 1;
-    if constexpr (MASK != MASK_NONE) kv_hi = q_last;
-    if constexpr (MASK == MASK_WINDOW) kv_lo = max(0, q_tile0 - p.window + 1);
-    const int t_begin = kv_lo / BN;
-    const int t_end = kv_hi / BN + 1;
-
-    // ---- two-term P for query tiles whose first row sees few keys
-    int min_vis = N;
-    if constexpr (MASK != MASK_NONE) min_vis = min(N, q_tile0 + 1);
-    if constexpr (MASK == MASK_WINDOW) min_vis = min(min_vis, p.window);
-    const bool exact = min_vis < p.exact_below;
-
-    f32x16 oacc[QB][CB];
-    float mrun[QB], lsum[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        mrun[qb] = -__builtin_inff();
-        lsum[qb] = 0.0f;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][cb][r] = 0.0f;
-    }
-
-    // ---- global -> LDS tile loader.  Each wave instruction fills 1 KiB of
-    // LDS linearly (lane * 16 B); the lane picks the global chunk that belongs
-    // at that swizzled LDS position.  Rows past N read row N-1 (finite data,
-    // masked later).
-    auto load_tile = [&](int t, int stage) {
+    // Issue the direct loads of tile t (keys t*BN ..) into ring stage dst.
+    static __device__ __forceinline__ void load_tile(const Ctx &x, int t, char *kdst, char *vdst) {
         const int j0 = t * BN;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int slot = (i * NW + wave) * 64 + lane;
+            const int slot = (i * NWQ + x.wave_q) * 64 + x.lane;
             const int row = slot / CHUNKS_PER_ROW;
             const int chp = slot % CHUNKS_PER_ROW;
             const int ch = chp ^ swz<D>(row);
-            const int64_t grow = min(j0 + row, N - 1);
+            const int64_t grow = min(j0 + row, x.N - 1);
             const int64_t off = grow * D + ch * 8;
-            ATTN_LDS void *kd = (ATTN_LDS void *)(&smem[stage][0][(i * NW + wave) * 1024]);
-            ATTN_LDS void *vd = (ATTN_LDS void *)(&smem[stage][1][(i * NW + wave) * 1024]);
-            __builtin_amdgcn_global_load_lds((const void *)(kp + off), kd, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vp + off), vd, 16, 0, 0);
+            const int lds_off = x.kgroup * TILEB + (i * NWQ + x.wave_q) * 1024;
+            __builtin_amdgcn_global_load_lds((const void *)(x.kp + off), (ATTN_LDS void *)(kdst + lds_off), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(x.vp + off), (ATTN_LDS void *)(vdst + lds_off), 16, 0, 0);
         }
-    };
+    }
 
-    load_tile(t_begin, 0);
-    wait_vmem_all();
-    __syncthreads();
+    // V^T A-operand fragment for 16-key step ks and channel block cb: two
+    // transposing reads of 4 keys x 16 channels per 16-lane group.
+    static __device__ __forceinline__ u32x4 v_frag(const Ctx &x, const char *vl, int ks, int cb) {
+        const int hgrp = x.lane >> 4;
+        const int tt = x.lane & 15;
+        const int row0 = ks * 16 + 8 * (hgrp >> 1) + (tt >> 2);
+        const int colb = cb * 64 + 32 * (hgrp & 1) + 8 * (tt & 3);
+        const int ch = colb >> 4, within = colb & 15;
+        const ATTN_LDS char *v0 = (const ATTN_LDS char *)vl + row0 * ROWB + ((ch ^ swz<D>(row0)) << 4) + within;
+        const ATTN_LDS char *v1 = (const ATTN_LDS char *)vl + (row0 + 4) * ROWB + ((ch ^ swz<D>(row0 + 4)) << 4) + within;
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)v0);
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)v1);
+        const u32x2 a0 = __builtin_bit_cast(u32x2, t0);
+        const u32x2 a1 = __builtin_bit_cast(u32x2, t1);
+        return u32x4{a0[0], a0[1], a1[0], a1[1]};
+    }
 
-    const float c = p.c;
-    for (int t = t_begin; t < t_end; ++t) {
-        const int stage = (t - t_begin) & 1;
-        if (t + 1 < t_end) load_tile(t + 1, stage ^ 1);
-
-        const int j0 = t * BN;
-        bool any = wave_live;
-        if constexpr (MASK != MASK_NONE) any = any && (j0 <= w_last);
-        if constexpr (MASK == MASK_WINDOW) any = any && (j0 + BN - 1 >= qw0 - p.window + 1);
-
-        if (any) {
-            bool edge = (j0 + BN > N);
-            if constexpr (MASK != MASK_NONE) edge = edge || (j0 + BN - 1 > qw0);
-            if constexpr (MASK == MASK_WINDOW) edge = edge || (j0 < w_last - p.window + 1);
-
-            const char *kl = smem[stage][0];
-            const char *vl = smem[stage][1];
-
-            // ---- S^T = K . Q^T
-            f32x16 s[KB][QB];
+    // O^T += V^T . P^T over one tile (P_lo as well when EXACT).  The reads of
+    // step ks+1 are scheduled ahead of the MFMAs of step ks.
+    template <bool EXACT>
+    static __device__ __forceinline__ void pv(const Ctx &x, State &st, const char *vl,
+                                              const u32x4 (&ph)[QB][KS], const u32x4 (&pl)[QB][KS]) {
+        u32x4 va[KS][CB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
+            for (int cb = 0; cb < CB; ++cb) va[ks][cb] = v_frag(x, vl, ks, cb);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.0f;
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int kk = 0; kk < KT; ++kk) {
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const int row = kb * 32 + key_perm(l32);
-                    const int ch = (2 * kk + g) ^ swz<D>(row);
-                    const u32x4 a = *(const ATTN_LDS u32x4 *)((const ATTN_LDS char *)kl + row * ROWB + ch * 16);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32<DT>(a, qf[qb][kk], s[kb][qb]);
+                for (int qb = 0; qb < QB; ++qb) {
+                    st.oacc[qb][cb] = mfma32<DT>(va[ks][cb], ph[qb][ks], st.oacc[qb][cb]);
+                    if constexpr (EXACT) st.oacc[qb][cb] = mfma32<DT>(va[ks][cb], pl[qb][ks], st.oacc[qb][cb]);
                 }
-            }
+        constexpr int RD = 2 * CB;                        // transposing reads per step
+        constexpr int MF = CB * QB * (EXACT ? 2 : 1);     // MFMAs per step
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 1);
+        }
+    }
 
-            // ---- online softmax, one lane per query row
-            u32x4 ph[QB][KS], pl[QB][KS];
+    // Everything one wave does with one landed tile.
+    template <bool EXACT>
+    static __device__ __forceinline__ void compute_tile(const Ctx &x, State &st, int t, const char *kl,
+                                                        const char *vl) {
+        const int j0 = t * BN;
+        const int N = x.N;
+        bool edge = (j0 + BN > N);
+        if constexpr (MASK != MASK_NONE) edge = edge || (j0 + BN - 1 > x.qw0);
+        if constexpr (MASK == MASK_WINDOW) edge = edge || (j0 < x.w_last - x.window + 1);
+
+        // ---- S^T = K . Q^T; K fragments are read two d-steps ahead
+        f32x16 s[KB][QB];
+        u32x4 ka[KT][KB];
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int row = kb * 32 + key_perm(x.l32);
+                const int ch = (2 * kk + x.g) ^ swz<D>(row);
+                ka[kk][kb] = *(const ATTN_LDS u32x4 *)((const ATTN_LDS char *)kl + row * ROWB + ch * 16);
+            }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const int qi = qw0 + qb * 32 + l32;
+                f32x16 acc = {};
+#pragma unroll
+                for (int kk = 0; kk < KT; ++kk) acc = mfma32<DT>(ka[kk][kb], st.qf[qb][kk], acc);
+                s[kb][qb] = acc;
+            }
+        {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk) {
+                if (kk + 2 < KT) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, KB * QB, 0);
+            }
+        }
+
+        // ---- online softmax, one lane per query row
+        u32x4 ph[QB][KS], pl[QB][KS];
+        const float c = x.c;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (edge) {
+                const int qi = x.qw0 + qb * 32 + x.l32;
                 // visible iff lo <= key offset <= hi, offsets relative to j0 + 8g
-                int hi = N - 1 - (j0 + 8 * g);
+                int hi = N - 1 - (j0 + 8 * x.g);
                 int lo = -(1 << 30);
-                if (edge) {
-                    if constexpr (MASK != MASK_NONE) hi = min(hi, qi - (j0 + 8 * g));
-                    if constexpr (MASK == MASK_WINDOW) lo = qi - p.window + 1 - (j0 + 8 * g);
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int off = kb * 32 + 16 * (r / 8) + (r % 8);
-                            if (off > hi || off < lo) s[kb][qb][r] = -__builtin_inff();
-                        }
-                }
-                float mx = -__builtin_inff();
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-                mx = max_halves(mx);
-                const float mxc = mx * c;
-                const bool need = mxc > mrun[qb] + TAU;
-                if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                    const float alpha = need ? __builtin_amdgcn_exp2f(mrun[qb] - mxc) : 1.0f;
-                    mrun[qb] = need ? mxc : mrun[qb];
-                    lsum[qb] *= alpha;
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
-                }
-                // a row that has seen no key yet keeps m = -inf; use 0 so that
-                // masked scores (-inf) still give p = 0
-                const float msub = (mrun[qb] == -__builtin_inff()) ? 0.0f : mrun[qb];
-                float rs = 0.0f;
+                if constexpr (MASK != MASK_NONE) hi = min(hi, qi - (j0 + 8 * x.g));
+                if constexpr (MASK == MASK_WINDOW) lo = qi - x.window + 1 - (j0 + 8 * x.g);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c, -msub));
-                        s[kb][qb][r] = e;
-                        rs += e;
+                        const int off = kb * 32 + 16 * (r / 8) + (r % 8);
+                        if (off > hi || off < lo) s[kb][qb][r] = -__builtin_inff();
                     }
-                lsum[qb] += rs;
+            }
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+            mx = max_halves(mx);
+            const float mxc = mx * c;
+            const bool need = mxc > st.mrun[qb] + TAU;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(st.mrun[qb] - mxc) : 1.0f;
+                st.mrun[qb] = need ? mxc : st.mrun[qb];
+                st.lsum[qb] *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) st.oacc[qb][cb][r] *= alpha;
+            }
+            // a row that has seen no key yet keeps m = -inf; use 0 so that
+            // masked scores (-inf) still give p = 0
+            const float msub = (st.mrun[qb] == -__builtin_inff()) ? 0.0f : st.mrun[qb];
+            float rs = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c, -msub));
+                    s[kb][qb][r] = e;
+                    rs += e;
+                }
+            st.lsum[qb] += rs;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kb = ks / 2, r0 = 8 * (ks % 2);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    ph[qb][ks][w] = pack2<DT>(s[kb][qb][r0 + 2 * w], s[kb][qb][r0 + 2 * w + 1]);
+            }
+            if constexpr (EXACT) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int kb = ks / 2, r0 = 8 * (ks % 2);
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        ph[qb][ks][w] = pack2<DT>(s[kb][qb][r0 + 2 * w], s[kb][qb][r0 + 2 * w + 1]);
-                }
-                if (exact) {
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int kb = ks / 2, r0 = 8 * (ks % 2);
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            const uint32_t hw = ph[qb][ks][w];
-                            pl[qb][ks][w] = pack2<DT>(s[kb][qb][r0 + 2 * w] - lo_half<DT>(hw),
-                                                      s[kb][qb][r0 + 2 * w + 1] - hi_half<DT>(hw));
-                        }
-                    }
-                }
-            }
-
-            // ---- O^T += V^T . P^T
-            const int hgrp = lane >> 4;
-            const int tt = lane & 15;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const int row0 = ks * 16 + 8 * (hgrp >> 1) + (tt >> 2);
-                    const int colb = cb * 64 + 32 * (hgrp & 1) + 8 * (tt & 3);
-                    const int ch = colb >> 4, within = colb & 15;
-                    const ATTN_LDS char *v0 = (const ATTN_LDS char *)vl + row0 * ROWB +
-                                              ((ch ^ swz<D>(row0)) << 4) + within;
-                    const ATTN_LDS char *v1 = (const ATTN_LDS char *)vl + (row0 + 4) * ROWB +
-                                              ((ch ^ swz<D>(row0 + 4)) << 4) + within;
-                    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)v0);
-                    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)v1);
-                    const u32x2 a0 = __builtin_bit_cast(u32x2, t0);
-                    const u32x2 a1 = __builtin_bit_cast(u32x2, t1);
-                    const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        oacc[qb][cb] = mfma32<DT>(a, ph[qb][ks], oacc[qb][cb]);
-                        if (exact) oacc[qb][cb] = mfma32<DT>(a, pl[qb][ks], oacc[qb][cb]);
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t hw = ph[qb][ks][w];
+                        pl[qb][ks][w] = pack2<DT>(s[kb][qb][r0 + 2 * w] - lo_half<DT>(hw),
+                                                  s[kb][qb][r0 + 2 * w + 1] - hi_half<DT>(hw));
                     }
                 }
             }
         }
 
-        wait_vmem_all();
-        __syncthreads();
+        // ---- O^T += V^T . P^T
+        pv<EXACT>(x, st, vl, ph, pl);
     }
 
-    // ---- epilogue: O = acc / l, rounded once; LSE = ln 2 * (m + log2 l)
+    // One pipeline step on ring stage S: wait for tile i, barrier, prefetch
+    // tile i + NSTAGE - 1 into the stage that held tile i - 1, compute tile i.
+    template <int S, bool EXACT>
+    static __device__ __forceinline__ void step(const Ctx &x, State &st, int i, int my_begin, int my_count) {
+        wait_tiles<LPT>(min(NSTAGE - 2, my_count - 1 - i));
+        __builtin_amdgcn_s_barrier();
+        constexpr int SN = (S + NSTAGE - 1) % NSTAGE;
+        if (i + NSTAGE - 1 < my_count) load_tile(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
+        if (i < my_count) {
+            const int t = my_begin + i;
+            bool any = x.qw0 < x.N;
+            if constexpr (MASK != MASK_NONE) any = any && (t * BN <= x.w_last);
+            if constexpr (MASK == MASK_WINDOW) any = any && (t * BN + BN - 1 >= x.qw0 - x.window + 1);
+            if (any)
+                compute_tile<EXACT>(x, st, t, x.kst[S] + x.kgroup * TILEB, x.vst[S] + x.kgroup * TILEB);
+        }
+    }
+
+    template <bool EXACT>
+    static __device__ __forceinline__ void loop(const Ctx &x, State &st, int half, int my_begin, int my_count) {
+        for (int i = 0; i < half; i += NSTAGE) {
+            step<0, EXACT>(x, st, i, my_begin, my_count);
+            if (i + 1 < half) step<1 % NSTAGE, EXACT>(x, st, i + 1, my_begin, my_count);
+            if constexpr (NSTAGE > 2)
+                if (i + 2 < half) step<2 % NSTAGE, EXACT>(x, st, i + 2, my_begin, my_count);
+            if constexpr (NSTAGE > 3)
+                if (i + 3 < half) step<3 % NSTAGE, EXACT>(x, st, i + 3, my_begin, my_count);
+        }
+    }
+
+    static __device__ __forceinline__ void run(const Params &p, char *const (&kst)[NSTAGE],
+                                               char *const (&vst)[NSTAGE], float *ml) {
+        Ctx x;
+        x.lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        x.wave_q = wave % NWQ;
+        x.kgroup = wave / NWQ;
+        x.g = x.lane >> 5;
+        x.l32 = x.lane & 31;
+        x.N = p.N;
+        x.window = p.window;
+        x.c = p.c;
+        for (int s = 0; s < NSTAGE; ++s) {
+            x.kst[s] = kst[s];
+            x.vst[s] = vst[s];
+        }
+        const int N = p.N;
+
+        // ---- which (batch*head, query tile) this workgroup owns; for masked
+        // runs the heaviest query tiles (most visible keys) are dispatched first.
+        const int bid = blockIdx.x;
+        const int bh = bid % p.n_bh;
+        const int rank = bid / p.n_bh;
+        const int qt = (MASK == MASK_NONE) ? rank : (p.n_qtiles - 1 - rank);
+        const int b = bh / p.Hq;
+        const int h = bh - b * p.Hq;
+        const int hkv = p.Hq / p.group;
+        const int64_t kvhead = (int64_t)b * hkv + h / p.group;
+        const uint16_t *qp = p.q + (int64_t)bh * N * D;
+        x.kp = p.k + kvhead * N * D;
+        x.vp = p.v + kvhead * N * D;
+
+        const int q_tile0 = qt * BM;
+        x.qw0 = q_tile0 + x.wave_q * QB * 32;
+        x.w_last = min(x.qw0 + QB * 32, N) - 1;
+
+        State st;
+        // ---- Q fragments (MFMA B operand): lane holds row qw0 + 32*qb + l32,
+        // channels 16*kk + 8*g .. +7.  Rows past N are zero.
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float lt = sum_halves(lsum[qb]);
-        const int qi = qw0 + qb * 32 + l32;
-        if (qi < N) {
-            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-            uint16_t *orow = p.o + ((int64_t)bh * N + qi) * D;
+        for (int qb = 0; qb < QB; ++qb) {
+            const int row = x.qw0 + qb * 32 + x.l32;
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (row < N) {
+                    v = *(const u32x4 *)(qp + (int64_t)row * D + kk * 16 + x.g * 8);
+                    v ^= p.qsign;
+                }
+                st.qf[qb][kk] = v;
+            }
+            st.mrun[qb] = -__builtin_inff();
+            st.lsum[qb] = 0.0f;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const int ch = cb * 32 + 8 * j4 + 4 * g;
-                    u32x2 w;
-                    w[0] = pack2<DT>(oacc[qb][cb][4 * j4 + 0] * inv, oacc[qb][cb][4 * j4 + 1] * inv);
-                    w[1] = pack2<DT>(oacc[qb][cb][4 * j4 + 2] * inv, oacc[qb][cb][4 * j4 + 3] * inv);
-                    *(u32x2 *)(orow + ch) = w;
+                for (int r = 0; r < 16; ++r) st.oacc[qb][cb][r] = 0.0f;
+        }
+
+        // ---- key tiles seen by the workgroup, split between the key groups
+        const int q_last = min(q_tile0 + BM, N) - 1;
+        int kv_lo = 0, kv_hi = N - 1;
+        if constexpr (MASK != MASK_NONE) kv_hi = q_last;
+        if constexpr (MASK == MASK_WINDOW) kv_lo = max(0, q_tile0 - p.window + 1);
+        const int t_begin = kv_lo / BN;
+        const int n_tiles = kv_hi / BN + 1 - t_begin;
+        const int half = (n_tiles + KSPLIT - 1) / KSPLIT;
+        const int my_begin = t_begin + x.kgroup * half;
+        const int my_count = max(0, min(half, n_tiles - x.kgroup * half));
+
+        // ---- two-term P for query tiles whose first row sees few keys
+        int min_vis = N;
+        if constexpr (MASK != MASK_NONE) min_vis = min(N, q_tile0 + 1);
+        if constexpr (MASK == MASK_WINDOW) min_vis = min(min_vis, p.window);
+        const bool exact = min_vis < p.exact_below;
+
+        // ---- prologue: the first NSTAGE-1 tiles in flight
+#pragma unroll
+        for (int s = 0; s < NSTAGE - 1; ++s)
+            if (s < my_count) load_tile(x, my_begin + s, x.kst[s], x.vst[s]);
+
+        // ---- main loop, unrolled over the ring stages; one instance per P mode
+        if (exact)
+            loop<true>(x, st, half, my_begin, my_count);
+        else
+            loop<false>(x, st, half, my_begin, my_count);
+
+        // ---- merge the key groups: group 1 hands (m, l, O) to group 0.  The
+        // ring is idle now; channel block cb of O goes to ring array cb.
+        if constexpr (KSPLIT == 2) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();
+            char *ring[2 * NSTAGE];
+#pragma unroll
+            for (int s2 = 0; s2 < NSTAGE; ++s2) {
+                ring[2 * s2] = x.kst[s2];
+                ring[2 * s2 + 1] = x.vst[s2];
+            }
+            if (x.kgroup == 1) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int base = (x.wave_q * QB + qb);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        float *dst = (float *)ring[cb];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) dst[(base * 16 + r) * 64 + x.lane] = st.oacc[qb][cb][r];
+                    }
+                    ml[(base * 2 + 0) * 64 + x.lane] = st.mrun[qb];
+                    ml[(base * 2 + 1) * 64 + x.lane] = st.lsum[qb];
                 }
-            if (p.lse != nullptr && g == 0) {
-                const float l2 = lt > 0.0f ? __builtin_amdgcn_logf(lt) : -__builtin_inff();
-                p.lse[(int64_t)bh * N + qi] = (mrun[qb] + l2) * 0.69314718055994530942f;
+            }
+            __syncthreads();
+            if (x.kgroup == 1) return;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int base = (x.wave_q * QB + qb);
+                const float m1 = ml[(base * 2 + 0) * 64 + x.lane];
+                const float l1 = ml[(base * 2 + 1) * 64 + x.lane];
+                const float m0 = st.mrun[qb];
+                const float m = fmaxf(m0, m1);
+                const float a0 = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
+                const float a1 = (m1 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+                st.mrun[qb] = m;
+                st.lsum[qb] = st.lsum[qb] * a0 + l1 * a1;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const float *src = (const float *)ring[cb];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        st.oacc[qb][cb][r] = st.oacc[qb][cb][r] * a0 + src[(base * 16 + r) * 64 + x.lane] * a1;
+                }
+            }
+        }
+
+        // ---- epilogue: O = acc / l, rounded once; LSE = ln 2 * (m + log2 l)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float lt = sum_halves(st.lsum[qb]);
+            const int qi = x.qw0 + qb * 32 + x.l32;
+            if (qi < N) {
+                const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+                uint16_t *orow = p.o + ((int64_t)bh * N + qi) * D;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const int ch = cb * 32 + 8 * j4 + 4 * x.g;
+                        u32x2 w;
+                        w[0] = pack2<DT>(st.oacc[qb][cb][4 * j4 + 0] * inv, st.oacc[qb][cb][4 * j4 + 1] * inv);
+                        w[1] = pack2<DT>(st.oacc[qb][cb][4 * j4 + 2] * inv, st.oacc[qb][cb][4 * j4 + 3] * inv);
+                        *(u32x2 *)(orow + ch) = w;
+                    }
+                if (p.lse != nullptr && x.g == 0) {
+                    const float l2 = lt > 0.0f ? __builtin_amdgcn_logf(lt) : -__builtin_inff();
+                    p.lse[(int64_t)bh * N + qi] = (st.mrun[qb] + l2) * 0.69314718055994530942f;
+                }
             }
         }
     }
+};
+
+// Ring-stage LDS objects are declared one by one so that each stage is a
+// distinct object to the compiler's alias analysis.
+template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
+__global__ __launch_bounds__(NWQ * KSPLIT * 64) void attn_fwd_kernel(Params p) {
+    using K = Kernel<D, DT, MASK, QB, NWQ, KSPLIT, BN, NSTAGE>;
+    constexpr int SB = K::STAGEB;
+    __shared__ __attribute__((aligned(1024))) char k0[SB];
+    __shared__ __attribute__((aligned(1024))) char v0[SB];
+    __shared__ __attribute__((aligned(1024))) char k1[SB];
+    __shared__ __attribute__((aligned(1024))) char v1[SB];
+    __shared__ __attribute__((aligned(1024))) char k2[NSTAGE > 2 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) char v2[NSTAGE > 2 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) char k3[NSTAGE > 3 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) char v3[NSTAGE > 3 ? SB : 16];
+    // the merge of two key groups keeps O in the ring and (m, l) here
+    static_assert(KSPLIT == 1 || (D / 32 <= 2 * NSTAGE && NWQ * QB * 16 * 64 * 4 <= SB),
+                  "ring too small to hold the key-group merge");
+    __shared__ __attribute__((aligned(16))) float ml[KSPLIT == 2 ? NWQ * QB * 2 * 64 : 4];
+    char *kst[NSTAGE];
+    char *vst[NSTAGE];
+    kst[0] = k0; vst[0] = v0;
+    kst[1] = k1; vst[1] = v1;
+    if constexpr (NSTAGE > 2) { kst[2] = k2; vst[2] = v2; }
+    if constexpr (NSTAGE > 3) { kst[3] = k3; vst[3] = v3; }
+    K::run(p, kst, vst, ml);
 }
 
 }  // namespace attnfwd

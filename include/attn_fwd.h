@@ -114,13 +114,14 @@ int attn_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int 
 
 /*
  * Tile configurations compiled into the library, for measurement: the count,
- * and for id in [0, count) the description desc[0..3] = {32-row query blocks
- * per wave, waves per workgroup, keys per K/V tile, query rows per
- * workgroup}.  attn_fwd_config_desc returns ATTN_ERR_ARG for a bad id or a
- * NULL desc.
+ * and for id in [0, count) and head dim d (64 or 128) the description
+ * desc[0..5] = {32-row query blocks per wave, waves per workgroup, keys per
+ * K/V tile, query rows per workgroup, key groups per workgroup, depth of the
+ * LDS tile ring}.  attn_fwd_config_desc returns ATTN_ERR_ARG for a bad id, a
+ * bad d or a NULL desc.
  */
 int attn_fwd_num_configs(void);
-int attn_fwd_config_desc(int id, int64_t *desc);
+int attn_fwd_config_desc(int id, int64_t d, int64_t *desc);
 
 /*
  * attn_fwd_plan for a given configuration id (-1 = the automatic choice);

@@ -82,13 +82,17 @@ def test_plan_reports_tiles():
     assert fa.attn_fwd_plan(1, 1, 1, 100, 64, 0, 0, 0)["exact_tiles"] == 1   # short non-causal rows
     assert fa.attn_fwd_plan(1, 1, 1, 5000, 64, 0, 0, 0)["exact_tiles"] == 0
     assert fa.attn_fwd_plan(1, 32, 1, 32768, 128, 1, 4096, 1)["mask_mode"] == 2
-    for cid in range(fa.attn_fwd_num_configs()):
-        desc = fa.attn_fwd_config_desc(cid)
-        assert desc["block_m"] == 32 * desc["query_blocks_per_wave"] * desc["waves"]
-        pe = fa.attn_fwd_plan_ex(2, 4, 4, 1000, 64, 1, 0, 0, cid)
-        assert pe["config_id"] == cid and pe["block_m"] == desc["block_m"]
+    for d in (64, 128):
+        for cid in range(fa.attn_fwd_num_configs()):
+            desc = fa.attn_fwd_config_desc(cid, d)
+            assert desc["block_m"] * desc["key_groups"] == 32 * desc["query_blocks_per_wave"] * desc["waves"]
+            pe = fa.attn_fwd_plan_ex(2, 4, 4, 1000, d, 1, 0, 0, cid)
+            assert pe["config_id"] == cid and pe["block_m"] == desc["block_m"]
+            assert pe["block_n"] == desc["block_n"] and pe["waves"] == desc["waves"]
     with pytest.raises(fa.AttnError):
         fa.attn_fwd_config_desc(fa.attn_fwd_num_configs())
+    with pytest.raises(fa.AttnError):
+        fa.attn_fwd_config_desc(0, 96)
     with pytest.raises(fa.AttnError):
         fa.attn_fwd_plan(1, 3, 2, 10, 64, 1, 0, 0)
 
