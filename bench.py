@@ -39,6 +39,8 @@ WORKLOAD_SETS = {
     "mqa": ["mqa_window", "mqa_causal"],
     "mqa_window": ["mqa_window"],
     "lab4096": ["lab_n4096_full", "lab_n4096_causal"],
+    "lab_n4096_full": ["lab_n4096_full"],
+    "mqa_causal": ["mqa_causal"],
 }
 
 
@@ -131,6 +133,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=-1, help="tile configuration id (-1: automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device-to-device copies of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -146,8 +150,18 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
-    fa.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": max(1, args.steps)}), flush=True)
+        return 0
+    fa.load_library()
     stream = torch.cuda.current_stream(dev)
     wls = [WORKLOADS[n] for n in WORKLOAD_SETS[args.workload]]
 

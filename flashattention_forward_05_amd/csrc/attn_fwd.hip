@@ -10,6 +10,7 @@
 
 #include "attn_fwd.h"
 #include "attn_fwd_kernel.hpp"
+#include "attn_fwd_pingpong.hpp"
 
 namespace {
 
@@ -18,25 +19,31 @@ using attnfwd::Params;
 // Tile configurations compiled into the library.  qb: 32-row query blocks
 // per wave; nwq: query waves per workgroup; ksplit: key groups per workgroup
 // (2 = a second set of waves takes the second half of the key range, merged
-// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring.  The
-// same id may use a smaller tile for d = 128 so that LDS stays within 160 KiB.
+// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring;
+// pingpong: the two wave groups alternate matrix and vector phases (then
+// ksplit = 1 means the groups own different query rows).  The same id may use
+// a smaller tile for d = 128 so that LDS stays within 160 KiB.
 struct TileCfg {
-    int qb, nwq, ksplit, bn, nstage;
+    int qb, nwq, ksplit, bn, nstage, pingpong;
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 4;
+constexpr int kNumConfigs = 6;
 constexpr TileCfg kCfg64[kNumConfigs] = {
-    {1, 4, 1, 64, 3},   // 0: 128 rows, 4 waves
-    {1, 4, 2, 64, 3},   // 1: 128 rows, 8 waves (two key groups)
-    {1, 8, 1, 64, 3},   // 2: 256 rows, 8 waves
-    {2, 4, 1, 64, 3},   // 3: 256 rows, 4 waves with 64 rows each
+    {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
+    {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
+    {1, 8, 1, 64, 3, 0},   // 2: 256 rows, 8 waves
+    {2, 4, 1, 64, 3, 0},   // 3: 256 rows, 4 waves with 64 rows each
+    {1, 8, 1, 64, 4, 1},   // 4: ping-pong, 256 rows in two row groups
+    {1, 4, 2, 64, 4, 1},   // 5: ping-pong, 128 rows, two key groups
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
-    {1, 4, 1, 64, 3},
-    {1, 4, 2, 64, 2},
-    {1, 8, 1, 64, 3},
-    {2, 4, 1, 64, 3},
+    {1, 4, 1, 64, 3, 0},
+    {1, 4, 2, 64, 2, 0},
+    {1, 8, 1, 64, 3, 0},
+    {2, 4, 1, 64, 3, 0},
+    {1, 8, 1, 64, 4, 1},
+    {1, 4, 2, 32, 4, 1},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
@@ -85,6 +92,14 @@ hipError_t launch_one(const Params &p, int64_t grid, hipStream_t stream) {
                            dim3((unsigned)grid), dim3(NWQ * KSPLIT * 64), argv, 0, stream);
 }
 
+template <int D, int DT, int MASK, int NWG, bool ROWS, int BN>
+hipError_t launch_pp(const Params &p, int64_t grid, hipStream_t stream) {
+    Params args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_pingpong_kernel<D, DT, MASK, NWG, ROWS, BN>,
+                           dim3((unsigned)grid), dim3(2 * NWG * 64), argv, 0, stream);
+}
+
 template <int D, int DT, int MASK>
 hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
     constexpr bool small = D == 64;
@@ -93,6 +108,8 @@ hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream
     case 1: return launch_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2>(p, grid, stream);
     case 2: return launch_one<D, DT, MASK, 1, 8, 1, 64, 3>(p, grid, stream);
     case 3: return launch_one<D, DT, MASK, 2, 4, 1, 64, 3>(p, grid, stream);
+    case 4: return launch_pp<D, DT, MASK, 4, true, 64>(p, grid, stream);
+    case 5: return launch_pp<D, DT, MASK, 4, false, small ? 64 : 32>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1,0 +1,222 @@
+// attn_fwd_common.hpp -- pieces shared by the attention-forward kernels for
+// gfx950: parameter block, MFMA and conversion wrappers, cross-half lane
+// reductions, the K row order of the S^T MFMA, the LDS swizzle and the
+// vector-memory wait helpers.  The layout facts these rely on are described in
+// attn_fwd_kernel.hpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfwd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+enum { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_WINDOW = 2 };
+
+// Raise the running max only when a row's new max exceeds it by more than
+// this many powers of two.
+constexpr float TAU = 8.0f;
+
+struct Params {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    uint16_t *o;
+    float *lse;          // may be null
+    int Hq;
+    int N;
+    int group;           // Hq / Hkv
+    int window;          // > 0 only with MASK_WINDOW
+    int n_qtiles;        // ceil(N / BM)
+    int n_bh;            // B * Hq
+    int exact_below;     // a q-tile whose first row sees fewer keys uses two-term P
+    float c;             // |scale| * log2(e), at least 2^-100
+    uint32_t qsign;      // 0x80008000 when scale < 0 (flips the sign of Q), else 0
+};
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 acc) {
+    if constexpr (DT == 0)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// Two fp32 values to a packed pair of 16-bit values, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+    if constexpr (DT == 0) {
+        f16x2 h = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(uint32_t, h);
+    } else {
+        bf16x2 h = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, h);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float lo_half(uint32_t u) {
+    if constexpr (DT == 0)
+        return (float)__builtin_bit_cast(f16x2, u)[0];
+    else
+        return __uint_as_float(u << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float hi_half(uint32_t u) {
+    if constexpr (DT == 0)
+        return (float)__builtin_bit_cast(f16x2, u)[1];
+    else
+        return __uint_as_float(u & 0xffff0000u);
+}
+
+// Max / sum of a value over lanes l and l ^ 32.
+__device__ __forceinline__ float max_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row order of K in the QK^T A operand: bits 2 and 3 exchanged.
+__device__ __forceinline__ int key_perm(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// XOR swizzle of the 16-byte chunk index within a K/V row in LDS.  For D=128
+// a row is 256 B (all 64 banks); for D=64 two rows share the 64 banks.  The
+// choice makes both the MFMA A-operand reads of K (16 consecutive rows, same
+// chunk) and the transposing reads of V (4 consecutive rows x 4 chunks per
+// half-wave) touch distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128)
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    else
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// s_waitcnt immediate with only the vector-memory counter constrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most `younger` tiles (of LPT loads each) of this wave are
+// still in flight.
+template <int LPT>
+__device__ __forceinline__ void wait_tiles(int younger) {
+    if (younger >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+    else if (younger == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+// Online-softmax update of one wave's tile of scores.  s holds S^T for KB
+// blocks of 32 keys (lane = query row, register r of block kb = key
+// 32*kb + 16*(r/8) + 8*g + (r%8)); m and l are the row's running max (log2
+// units, scaled by c) and its lane-half share of the running sum; o is the
+// O^T accumulator.  Writes the packed 16-bit P^T (and for EXACT the rounding
+// residual P_lo) in the B-operand layout of O^T += V^T . P^T.
+//
+// Steady state skips the tile max: p = 2^(s*c - m) against the running max,
+// accepted when every lane-half sum stays <= 2^15 (so every p fits the 16-bit
+// P and nothing overflows); this is the same algebra with a stale reference
+// point, as exact as the rescaled form.  Otherwise -- first tile of a row,
+// tiles that cut a mask, two-term P, or a sum out of range -- the tile max is
+// taken, m is raised when it grows by more than TAU, and O and l are rescaled.
+// On edge tiles a key is visible iff lo <= (key offset from j0 + 8g) <= hi.
+template <int DT, int KB, int CB, bool EXACT>
+__device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], f32x16 (&o)[CB], float &m, float &l,
+                                               u32x4 (&ph)[2 * KB], u32x4 (&pl)[2 * KB], float c,
+                                               bool edge, int hi, int lo) {
+    if constexpr (!EXACT) {
+        if (!edge && __builtin_amdgcn_ballot_w64(m == -__builtin_inff()) == 0) {
+            float rs = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 2 * KB; ++ks) {
+                const int kb = ks / 2, r0 = 8 * (ks % 2);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * q], c, -m));
+                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * q + 1], c, -m));
+                    rs += e0;
+                    rs += e1;
+                    ph[ks][q] = pack2<DT>(e0, e1);
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(!(rs <= 32768.0f)) == 0) {
+                l += rs;
+                return;
+            }
+        }
+    }
+    if (edge) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = kb * 32 + 16 * (r / 8) + (r % 8);
+                if (off > hi || off < lo) s[kb][r] = -__builtin_inff();
+            }
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_halves(mx);
+    const float mxc = mx * c;
+    const bool need = mxc > m + TAU;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
+        m = need ? mxc : m;
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+    }
+    // a row that has seen no key yet keeps m = -inf; use 0 so that masked
+    // scores (-inf) still give p = 0
+    const float msub = (m == -__builtin_inff()) ? 0.0f : m;
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -msub));
+            s[kb][r] = e;
+            rs += e;
+        }
+    l += rs;
+#pragma unroll
+    for (int ks = 0; ks < 2 * KB; ++ks) {
+        const int kb = ks / 2, r0 = 8 * (ks % 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t hw = pack2<DT>(s[kb][r0 + 2 * q], s[kb][r0 + 2 * q + 1]);
+            ph[ks][q] = hw;
+            if constexpr (EXACT)
+                pl[ks][q] = pack2<DT>(s[kb][r0 + 2 * q] - lo_half<DT>(hw), s[kb][r0 + 2 * q + 1] - hi_half<DT>(hw));
+        }
+    }
+}
+
+}  // namespace attnfwd

@@ -38,10 +38,12 @@
 //    bare s_barrier.  16-byte chunks are XOR-swizzled per row so that the
 //    MFMA-operand reads of 16 consecutive rows hit distinct LDS banks.
 //  * Softmax runs in base 2: c = |scale| * log2(e) is folded into one FMA per
-//    score, p = v_exp_f32(s*c - m).  The running max m is only raised when a
-//    row's new max exceeds it by more than TAU (log2 units); p is then at most
-//    2^TAU, harmless in fp32 and in the 16-bit P, and the O rescale (an
-//    exact algebraic no-op otherwise) is skipped for most tiles.
+//    score, p = v_exp_f32(s*c - m).  In steady state the tile max is not even
+//    taken: p is formed against the running max and accepted while every
+//    partial row sum stays <= 2^15; otherwise the tile max is taken and the
+//    running max raised when it grows by more than TAU (log2 units).  Both are
+//    the same algebra with a different reference point, so the O rescale is
+//    skipped for most tiles (online_softmax in attn_fwd_common.hpp).
 //  * Query tiles whose first row sees few keys use a two-term P (P_hi + P_lo,
 //    both rounded to the 16-bit dtype, two MFMAs) so that the rounding of P
 //    does not dominate the error of rows that average only a few values.
@@ -49,128 +51,9 @@
 //    causal diagonal, the window edge or the ragged tail evaluate masks.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "attn_fwd_common.hpp"
 
 namespace attnfwd {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-#define ATTN_LDS __attribute__((address_space(3)))
-
-enum { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_WINDOW = 2 };
-
-// Raise the running max only when a row's new max exceeds it by more than
-// this many powers of two.
-constexpr float TAU = 8.0f;
-
-struct Params {
-    const uint16_t *q;
-    const uint16_t *k;
-    const uint16_t *v;
-    uint16_t *o;
-    float *lse;          // may be null
-    int Hq;
-    int N;
-    int group;           // Hq / Hkv
-    int window;          // > 0 only with MASK_WINDOW
-    int n_qtiles;        // ceil(N / BM)
-    int n_bh;            // B * Hq
-    int exact_below;     // a q-tile whose first row sees fewer keys uses two-term P
-    float c;             // |scale| * log2(e), at least 2^-100
-    uint32_t qsign;      // 0x80008000 when scale < 0 (flips the sign of Q), else 0
-};
-
-template <int DT>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 acc) {
-    if constexpr (DT == 0)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
-
-// Two fp32 values to a packed pair of 16-bit values, round to nearest even.
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-    if constexpr (DT == 0) {
-        f16x2 h = {(_Float16)x, (_Float16)y};
-        return __builtin_bit_cast(uint32_t, h);
-    } else {
-        bf16x2 h = {(__bf16)x, (__bf16)y};
-        return __builtin_bit_cast(uint32_t, h);
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ float lo_half(uint32_t u) {
-    if constexpr (DT == 0)
-        return (float)__builtin_bit_cast(f16x2, u)[0];
-    else
-        return __uint_as_float(u << 16);
-}
-
-template <int DT>
-__device__ __forceinline__ float hi_half(uint32_t u) {
-    if constexpr (DT == 0)
-        return (float)__builtin_bit_cast(f16x2, u)[1];
-    else
-        return __uint_as_float(u & 0xffff0000u);
-}
-
-// Max / sum of a value over lanes l and l ^ 32.
-__device__ __forceinline__ float max_halves(float x) {
-    uint32_t u = __float_as_uint(x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float sum_halves(float x) {
-    uint32_t u = __float_as_uint(x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Row order of K in the QK^T A operand: bits 2 and 3 exchanged.
-__device__ __forceinline__ int key_perm(int m) {
-    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-// XOR swizzle of the 16-byte chunk index within a K/V row in LDS.  For D=128
-// a row is 256 B (all 64 banks); for D=64 two rows share the 64 banks.  The
-// choice makes both the MFMA A-operand reads of K (16 consecutive rows, same
-// chunk) and the transposing reads of V (4 consecutive rows x 4 chunks per
-// half-wave) touch distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128)
-        return ((row & 3) << 2) | ((row >> 2) & 3);
-    else
-        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-// s_waitcnt immediate with only the vector-memory counter constrained.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Wait until at most `younger` tiles (of LPT loads each) of this wave are
-// still in flight.
-template <int LPT>
-__device__ __forceinline__ void wait_tiles(int younger) {
-    if (younger >= 2)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
-    else if (younger == 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-    else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-}
 
 template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
 struct Kernel {
@@ -294,12 +177,13 @@ struct Kernel {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                f32x16 acc = {};
+            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
 #pragma unroll
-                for (int kk = 0; kk < KT; ++kk) acc = mfma32<DT>(ka[kk][kb], st.qf[qb][kk], acc);
-                s[kb][qb] = acc;
-            }
+        for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32<DT>(ka[kk][kb], st.qf[qb][kk], s[kb][qb]);
         {
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
 #pragma unroll
@@ -311,73 +195,18 @@ struct Kernel {
 
         // ---- online softmax, one lane per query row
         u32x4 ph[QB][KS], pl[QB][KS];
-        const float c = x.c;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            if (edge) {
-                const int qi = x.qw0 + qb * 32 + x.l32;
-                // visible iff lo <= key offset <= hi, offsets relative to j0 + 8g
-                int hi = N - 1 - (j0 + 8 * x.g);
-                int lo = -(1 << 30);
-                if constexpr (MASK != MASK_NONE) hi = min(hi, qi - (j0 + 8 * x.g));
-                if constexpr (MASK == MASK_WINDOW) lo = qi - x.window + 1 - (j0 + 8 * x.g);
+            const int qi = x.qw0 + qb * 32 + x.l32;
+            int hi = N - 1 - (j0 + 8 * x.g);
+            int lo = -(1 << 30);
+            if constexpr (MASK != MASK_NONE) hi = min(hi, qi - (j0 + 8 * x.g));
+            if constexpr (MASK == MASK_WINDOW) lo = qi - x.window + 1 - (j0 + 8 * x.g);
+            f32x16 sq[KB];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int off = kb * 32 + 16 * (r / 8) + (r % 8);
-                        if (off > hi || off < lo) s[kb][qb][r] = -__builtin_inff();
-                    }
-            }
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-            mx = max_halves(mx);
-            const float mxc = mx * c;
-            const bool need = mxc > st.mrun[qb] + TAU;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float alpha = need ? __builtin_amdgcn_exp2f(st.mrun[qb] - mxc) : 1.0f;
-                st.mrun[qb] = need ? mxc : st.mrun[qb];
-                st.lsum[qb] *= alpha;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) st.oacc[qb][cb][r] *= alpha;
-            }
-            // a row that has seen no key yet keeps m = -inf; use 0 so that
-            // masked scores (-inf) still give p = 0
-            const float msub = (st.mrun[qb] == -__builtin_inff()) ? 0.0f : st.mrun[qb];
-            float rs = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c, -msub));
-                    s[kb][qb][r] = e;
-                    rs += e;
-                }
-            st.lsum[qb] += rs;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kb = ks / 2, r0 = 8 * (ks % 2);
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    ph[qb][ks][w] = pack2<DT>(s[kb][qb][r0 + 2 * w], s[kb][qb][r0 + 2 * w + 1]);
-            }
-            if constexpr (EXACT) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int kb = ks / 2, r0 = 8 * (ks % 2);
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const uint32_t hw = ph[qb][ks][w];
-                        pl[qb][ks][w] = pack2<DT>(s[kb][qb][r0 + 2 * w] - lo_half<DT>(hw),
-                                                  s[kb][qb][r0 + 2 * w + 1] - hi_half<DT>(hw));
-                    }
-                }
-            }
+            for (int kb = 0; kb < KB; ++kb) sq[kb] = s[kb][qb];
+            online_softmax<DT, KB, CB, EXACT>(sq, st.oacc[qb], st.mrun[qb], st.lsum[qb], ph[qb], pl[qb], x.c,
+                                              edge, hi, lo);
         }
 
         // ---- O^T += V^T . P^T
