@@ -84,8 +84,10 @@ def traffic_from_profiles(kernel_label: str):
 
 
 def cpu_baseline(workloads, budget_s: float):
-    """The oracle, untuned, on every stride-th query row of each variant, in
-    chunks until the time budget is spent; reports the achieved rate."""
+    """The oracle, untuned, on a seeded random sample of query rows of each
+    variant, in chunks of 64 rows until that variant's share of the time
+    budget is spent; reports the achieved rate in the metric's unit (FLOPs
+    counted per row: 4*d per visible key)."""
     import numpy as np
 
     import oracle
@@ -95,19 +97,18 @@ def cpu_baseline(workloads, budget_s: float):
     flops = 0.0
     elapsed = 0.0
     rows_done = 0
-    stride = 16
     per_variant = budget_s / len(workloads)
+    rng = np.random.default_rng(0)
     for w in workloads:
         q, k, v = (to_bits(t) for t in make_workload(w, seed=0))
-        ids = np.arange(0, w.B * w.Hq * w.N, stride, dtype=np.int64)
+        ids = rng.permutation(w.B * w.Hq * w.N).astype(np.int64)
         t_var = 0.0
         for start in range(0, len(ids), 64):
             chunk = ids[start:start + 64]
             t0 = time.perf_counter()
             oracle.oracle_rows(q, k, v, chunk, scale=float(np.float32(w.scale)), causal=w.causal,
                                window=w.window, dtype=w.dtype)
-            dt = time.perf_counter() - t0
-            t_var += dt
+            t_var += time.perf_counter() - t0
             rows_done += len(chunk)
             flops += sum(4.0 * w.d * visible_keys(int(r) % w.N, w.N, w.causal, w.window) for r in chunk)
             if t_var > per_variant:
@@ -118,10 +119,67 @@ def cpu_baseline(workloads, budget_s: float):
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"fp64 oracle on every {stride}th query row of each variant "
-                   f"({rows_done} rows, {flops / 1e9:.2f} GFLOP, {elapsed:.1f} s, "
-                   f"about {per_variant:.0f} s per variant)"),
+        "sample": (f"fp64 oracle on random query rows of every variant, about {per_variant:.1f} s each "
+                   f"({rows_done} rows, {flops / 1e9:.2f} GFLOP in {elapsed:.1f} s)"),
     }
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> short text summaries for profiles/ (run on any host)
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(trace_dir: str) -> str:
+    """Per (kernel, grid) mean/min/max duration from a --kernel-trace CSV."""
+    import glob
+    import statistics
+    rows = _read_csv(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])
+    groups = {}
+    for r in rows:
+        if "attn_fwd" not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"], int(r["Grid_Size"]) if "Grid_Size" in r else int(r.get("Grid_Size_X", 0)))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["kernel | grid threads | launches | mean us | min us | max us"]
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -statistics.mean(kv[1])):
+        out.append(f"{name} | {grid} | {len(d)} | {statistics.mean(d):.2f} | {min(d):.2f} | {max(d):.2f}")
+    return "\n".join(out)
+
+
+def summarize_counters(dirs: dict) -> dict:
+    """Mean counter value per kernel over the dispatches of each pass."""
+    import glob
+    res = {}
+    for tag, d in dirs.items():
+        for r in _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0]):
+            k = (r["Kernel_Name"], r["Counter_Name"])
+            res.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in res.items()}
+
+
+def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, label):
+    """HBM bytes per launch of the attention kernel from FETCH_SIZE/WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a plain
+    copy of copy_mib MiB."""
+    f = summarize_counters({"f": fetch_dir})
+    w = summarize_counters({"w": write_dir})
+    cf = summarize_counters({"cf": copy_fetch_dir})
+    cw = summarize_counters({"cw": copy_write_dir})
+    known = copy_mib * (1 << 20)
+    cf_kib = max(v for (k, c), v in cf.items() if c == "FETCH_SIZE" and "copy" in k.lower())
+    cw_kib = max(v for (k, c), v in cw.items() if c == "WRITE_SIZE" and "copy" in k.lower())
+    fscale = known / (cf_kib * 1024)
+    wscale = known / (cw_kib * 1024)
+    kf = [v for (k, c), v in f.items() if c == "FETCH_SIZE" and "attn_fwd" in k][0]
+    kw = [v for (k, c), v in w.items() if c == "WRITE_SIZE" and "attn_fwd" in k][0]
+    return {"label": label, "fetch_kib_raw": kf, "write_kib_raw": kw, "fetch_scale": fscale,
+            "write_scale": wscale, "hbm_read_bytes": kf * 1024 * fscale,
+            "hbm_write_bytes": kw * 1024 * wscale,
+            "hbm_bytes_per_launch": kf * 1024 * fscale + kw * 1024 * wscale}
 
 
 def main() -> int:
@@ -135,7 +193,35 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (for scaling HBM counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="print a summary of a rocprofv3 kernel-trace CSV dir")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print mean counter values per kernel for rocprofv3 --pmc CSV dirs")
+    ap.add_argument("--traffic", nargs=6, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
+                                                   "COPY_MIB", "LABEL"),
+                    help="compute HBM bytes per launch from counter dirs and add it to profiles/traffic.json")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_counters:
+        vals = summarize_counters({d: d for d in args.summarize_counters})
+        for (k, c), v in sorted(vals.items()):
+            if "attn_fwd" in k:
+                print(f"{k} | {c} | {v:.6g}")
+        return 0
+    if args.traffic:
+        fd, wd, cfd, cwd, mib, label = args.traffic
+        rec = traffic_record(fd, wd, cfd, cwd, int(mib), label)
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        db = json.load(open(path)) if os.path.exists(path) else {}
+        if db.get("kernel_source_sha") != kernel_source_hash():
+            db = {"kernel_source_sha": kernel_source_hash(), "kernels": {}}
+        db["kernels"][label] = rec
+        with open(path, "w") as f:
+            json.dump(db, f, indent=1)
+        print(json.dumps(rec))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
