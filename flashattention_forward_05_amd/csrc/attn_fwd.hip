@@ -42,7 +42,7 @@ constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 2, 64, 2, 0},
     {1, 8, 1, 64, 3, 0},
     {2, 4, 1, 64, 3, 0},
-    {1, 8, 1, 64, 4, 1},
+    {1, 8, 1, 32, 4, 1},
     {1, 4, 2, 32, 4, 1},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
@@ -108,7 +108,7 @@ hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream
     case 1: return launch_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2>(p, grid, stream);
     case 2: return launch_one<D, DT, MASK, 1, 8, 1, 64, 3>(p, grid, stream);
     case 3: return launch_one<D, DT, MASK, 2, 4, 1, 64, 3>(p, grid, stream);
-    case 4: return launch_pp<D, DT, MASK, 4, true, 64>(p, grid, stream);
+    case 4: return launch_pp<D, DT, MASK, 4, true, small ? 64 : 32>(p, grid, stream);
     case 5: return launch_pp<D, DT, MASK, 4, false, small ? 64 : 32>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }

@@ -113,6 +113,34 @@ __device__ __forceinline__ int swz(int row) {
         return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
+// One 16-byte-per-lane direct load from global memory into LDS: lane i's 16
+// bytes land at lds_addr + 16 * i (lds_addr is wave-uniform).  Issued as
+// inline assembly so that the compiler does not treat it as an LDS store:
+// otherwise it waits for every such load in flight before any LDS read whose
+// target it cannot attribute to one LDS object, which cancels the
+// prefetching.  Completion is instead tracked by the explicit vmcnt waits in
+// the kernels, placed before the barrier that publishes a tile.  Nothing else
+// in these kernels uses m0.
+__device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_addr) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// LDS byte address of a pointer into an LDS object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
+}
+
+// Workgroup barrier with no memory-counter waits; the compiler may not move
+// memory accesses across it.
+__device__ __forceinline__ void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // s_waitcnt immediate with only the vector-memory counter constrained.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 

@@ -8,10 +8,12 @@
 // What differs is the schedule.
 //
 // Every wave works on one tile t in two phases:
-//   M_t : O^T += V^T . P^T for tile t-1, then S^T = K . Q^T for tile t
-//         (matrix cores only, plus LDS reads)
+//   M_t : O^T += V^T . P^T for tile t-1, then S^T = K . Q^T for tile t, on
+//         operands already in registers (matrix cores; for d = 128 the V^T
+//         operand is read here, the register file cannot hold it ahead)
 //   S_t : online softmax of S^T -> P^T, running max / sum, lazy O rescale
-//         (vector ALU only)
+//         (vector ALU), plus the LDS reads of K of tile t+1 (and for d = 64
+//         of V of tile t) for the next matrix phase
 // The workgroup holds two groups of NWG waves, one wave of each per SIMD.
 // Group A runs M_0 S_0 M_1 S_1 ...; group B runs the same sequence one
 // barrier later, so in every phase one group feeds the matrix cores of a SIMD
@@ -26,10 +28,14 @@
 //        the end with the rescale-and-add that "Optimizaciones de Atencion",
 //        section "FlashDecoding", uses to combine key chunks.  For small grids.
 //
-// The ring has four stages.  Around M_t a group's stages hold V of tile t-1
-// (being multiplied), K/V of tile t (being read), tile t+1 (landed or in
-// flight) and the stage of tile t-2, which is refilled with tile t+2 right
-// after the M_t barrier: two tile periods of load latency are hidden.
+// Putting every LDS read in the softmax phase spreads the operand traffic
+// evenly: with 32-row waves a matrix phase would otherwise ask LDS for about
+// as many bytes per clock as it delivers.
+//
+// The ring has four stages.  At M_t a group's stages hold tile t-1 and tile t
+// (already read into registers or being read in S_t), tile t+1 (landed before
+// S_t) and the stage of tile t-2, refilled with tile t+2 right after the M_t
+// barrier.
 #pragma once
 
 #include "attn_fwd_common.hpp"
@@ -53,6 +59,9 @@ struct PingPong {
     static constexpr int LPT = 2 * LOADS;
     static constexpr int RINGS = ROWS ? 1 : 2;
     static constexpr int STAGEB = RINGS * TILEB;          // bytes of one stage array
+    // V^T operands are read ahead in the softmax phase when registers allow
+    // (d = 64); for d = 128 the matrix phase reads them itself.
+    static constexpr bool VPRE = (D == 64);
     static_assert((BN * CPR) % (64 * NWG) == 0, "tile must split evenly over the loading waves");
     static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
 
@@ -74,6 +83,8 @@ struct PingPong {
         f32x16 o[CB];
         f32x16 s[KB];
         u32x4 ph[KS], pl[KS];
+        u32x4 ka[KT][KB];         // K operand of the next S^T, read during a softmax phase
+        u32x4 va[KS][CB];         // V^T operand of the next P.V, read during a softmax phase
         float m, l;
     };
 
@@ -95,37 +106,22 @@ struct PingPong {
             const int64_t grow = min(j0 + row, w.N - 1);
             const int64_t off = grow * D + ch * 8;
             const int lds_off = w.ring_off + (i * NWG + w.wq) * 1024;
-            __builtin_amdgcn_global_load_lds((const void *)(w.kp + off), (ATTN_LDS void *)(kdst + lds_off), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(w.vp + off), (ATTN_LDS void *)(vdst + lds_off), 16, 0, 0);
+            lds_dma16(w.kp + off, __builtin_amdgcn_readfirstlane(lds_addr(kdst + lds_off)));
+            lds_dma16(w.vp + off, __builtin_amdgcn_readfirstlane(lds_addr(vdst + lds_off)));
         }
     }
 
-    // S^T = K . Q^T for the tile in kl
-    static __device__ __forceinline__ void qk(const W &w, St &st, const char *kl) {
-        u32x4 ka[KT][KB];
+    // LDS -> registers: the K operand of a tile (kl) ...
+    static __device__ __forceinline__ void read_k(const W &w, St &st, const char *kl) {
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                ka[kk][kb] = *(const ATTN_LDS u32x4 *)((const ATTN_LDS char *)kl + w.koff[kk] + kb * 32 * ROWB);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) st.s[kb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) st.s[kb] = mfma32<DT>(ka[kk][kb], st.qf[kk], st.s[kb]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk) {
-            if (kk + 2 < KT) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
-        }
+                st.ka[kk][kb] = *(const ATTN_LDS u32x4 *)((const ATTN_LDS char *)kl + w.koff[kk] + kb * 32 * ROWB);
     }
 
-    // O^T += V^T . P^T for the tile in vl, with the P^T of that tile
-    template <bool EXACT>
-    static __device__ __forceinline__ void pv(const W &w, St &st, const char *vl) {
-        u32x4 va[KS][CB];
+    // ... and the V^T operand (vl), two transposing reads per fragment
+    static __device__ __forceinline__ void read_v(const W &w, St &st, const char *vl) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -135,23 +131,30 @@ struct PingPong {
                 const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)(b + w.voff[2 * cb + 1]));
                 const u32x2 a0 = __builtin_bit_cast(u32x2, t0);
                 const u32x2 a1 = __builtin_bit_cast(u32x2, t1);
-                va[ks][cb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                st.va[ks][cb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
             }
+    }
+
+    // S^T = K . Q^T from registers
+    static __device__ __forceinline__ void qk(St &st) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) st.s[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) st.s[kb] = mfma32<DT>(st.ka[kk][kb], st.qf[kk], st.s[kb]);
+    }
+
+    // O^T += V^T . P^T from registers (P_lo as well when EXACT)
+    template <bool EXACT>
+    static __device__ __forceinline__ void pv(St &st) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                st.o[cb] = mfma32<DT>(va[ks][cb], st.ph[ks], st.o[cb]);
-                if constexpr (EXACT) st.o[cb] = mfma32<DT>(va[ks][cb], st.pl[ks], st.o[cb]);
+                st.o[cb] = mfma32<DT>(st.va[ks][cb], st.ph[ks], st.o[cb]);
+                if constexpr (EXACT) st.o[cb] = mfma32<DT>(st.va[ks][cb], st.pl[ks], st.o[cb]);
             }
-        constexpr int RD = 2 * CB;
-        constexpr int MF = CB * (EXACT ? 2 : 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, MF, 1);
-        }
     }
 
     // online softmax of st.s (tile abs_tile) -> st.ph / st.pl
@@ -170,18 +173,29 @@ struct PingPong {
     }
 
     // One tile period: M_t then (unless t == T) S_t.  J = t mod 4 picks the
-    // ring stages at compile time.  Returns true after the last M phase.
+    // ring stages at compile time.  M_t touches no LDS: P.V of tile t-1 and
+    // S^T of tile t run on operands read during S_{t-1}.  S_t does the
+    // softmax of tile t and reads V of tile t and K of tile t+1.  Returns true
+    // after the last M phase.
     template <int J, bool EXACT>
     static __device__ __forceinline__ bool period(W &w, St &st, int t, bool &act_prev) {
-        if (w.loader && t < w.my_count) wait_tiles<LPT>(min(1, w.my_count - 1 - t));
-        __builtin_amdgcn_s_barrier();
+        block_sync();
         if (w.loader && t + 2 < w.my_count)
             load_tile(w, w.my_begin + t + 2, w.kst[(J + 2) % NSTAGE], w.vst[(J + 2) % NSTAGE]);
-        if (t >= 1 && act_prev) pv<EXACT>(w, st, w.vst[(J + 3) % NSTAGE] + w.ring_off);
+        if (t >= 1 && act_prev) {
+            if constexpr (!VPRE) read_v(w, st, w.vst[(J + 3) % NSTAGE] + w.ring_off);
+            pv<EXACT>(st);
+        }
         const bool cur = t < w.my_count && visible(w, w.my_begin + t);
-        if (cur) qk(w, st, w.kst[J] + w.ring_off);
+        if (cur) qk(st);
         if (t == w.T) return true;
-        __builtin_amdgcn_s_barrier();
+        // tile t+1 must have landed (tile t+2 may still be in flight)
+        if (w.loader && t + 1 < w.my_count) wait_tiles<LPT>(t + 2 < w.my_count ? 1 : 0);
+        block_sync();
+        if constexpr (VPRE)
+            if (cur) read_v(w, st, w.vst[J] + w.ring_off);
+        if (t + 1 < w.my_count && visible(w, w.my_begin + t + 1))
+            read_k(w, st, w.kst[(J + 1) % NSTAGE] + w.ring_off);
         if (cur) softmax<EXACT>(w, st, w.my_begin + t);
         act_prev = cur;
         return false;
@@ -190,14 +204,14 @@ struct PingPong {
     template <bool EXACT>
     static __device__ __forceinline__ void loop(W &w, St &st) {
         bool act_prev = false;
-        if (w.grp == 1) __builtin_amdgcn_s_barrier();      // group B runs one phase behind
+        if (w.grp == 1) block_sync();      // group B runs one phase behind
         for (int t = 0;; t += NSTAGE) {
             if (period<0, EXACT>(w, st, t, act_prev)) break;
             if (period<1, EXACT>(w, st, t + 1, act_prev)) break;
             if (period<2, EXACT>(w, st, t + 2, act_prev)) break;
             if (period<3, EXACT>(w, st, t + 3, act_prev)) break;
         }
-        if (w.grp == 0) __builtin_amdgcn_s_barrier();      // same barrier count as group B
+        if (w.grp == 0) block_sync();      // same barrier count as group B
     }
 
     static __device__ __forceinline__ void run(const Params &p, char *const (&kst)[NSTAGE],
@@ -301,7 +315,10 @@ struct PingPong {
         if (w.loader) {
             if (0 < w.my_count) load_tile(w, w.my_begin, w.kst[0], w.vst[0]);
             if (1 < w.my_count) load_tile(w, w.my_begin + 1, w.kst[1], w.vst[1]);
+            if (0 < w.my_count) wait_tiles<LPT>(1 < w.my_count ? 1 : 0);
         }
+        block_sync();
+        if (0 < w.my_count && visible(w, w.my_begin)) read_k(w, st, w.kst[0] + w.ring_off);
 
         if (exact)
             loop<true>(w, st);
