@@ -102,8 +102,8 @@ struct Kernel {
             const int64_t grow = min(j0 + row, x.N - 1);
             const int64_t off = grow * D + ch * 8;
             const int lds_off = x.kgroup * TILEB + (i * NWQ + x.wave_q) * 1024;
-            __builtin_amdgcn_global_load_lds((const void *)(x.kp + off), (ATTN_LDS void *)(kdst + lds_off), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(x.vp + off), (ATTN_LDS void *)(vdst + lds_off), 16, 0, 0);
+            lds_dma16(x.kp + off, __builtin_amdgcn_readfirstlane(lds_addr(kdst + lds_off)));
+            lds_dma16(x.vp + off, __builtin_amdgcn_readfirstlane(lds_addr(vdst + lds_off)));
         }
     }
 
@@ -218,7 +218,7 @@ struct Kernel {
     template <int S, bool EXACT>
     static __device__ __forceinline__ void step(const Ctx &x, State &st, int i, int my_begin, int my_count) {
         wait_tiles<LPT>(min(NSTAGE - 2, my_count - 1 - i));
-        __builtin_amdgcn_s_barrier();
+        block_sync();
         constexpr int SN = (S + NSTAGE - 1) % NSTAGE;
         if (i + NSTAGE - 1 < my_count) load_tile(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
         if (i < my_count) {
