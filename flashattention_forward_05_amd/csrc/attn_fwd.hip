@@ -10,6 +10,7 @@
 
 #include "attn_fwd.h"
 #include "attn_fwd_kernel.hpp"
+#include "attn_fwd_launch.hpp"
 #include "attn_fwd_pingpong.hpp"
 
 namespace {
@@ -19,16 +20,18 @@ using attnfwd::Params;
 // Tile configurations compiled into the library.  qb: 32-row query blocks
 // per wave; nwq: query waves per workgroup; ksplit: key groups per workgroup
 // (2 = a second set of waves takes the second half of the key range, merged
-// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring;
-// pingpong: the two wave groups alternate matrix and vector phases (then
-// ksplit = 1 means the groups own different query rows).  The same id may use
-// a smaller tile for d = 128 so that LDS stays within 160 KiB.
+// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring (of
+// each of the K and V rings for kind 2); kind: 0 = lockstep kernel, 1 =
+// ping-pong (the two wave groups alternate matrix and vector phases; then
+// ksplit = 1 means the groups own different query rows), 2 = in-wave
+// pipelined kernel.  The same id may use a smaller tile for d = 128 so that
+// LDS and registers fit.
 struct TileCfg {
-    int qb, nwq, ksplit, bn, nstage, pingpong;
+    int qb, nwq, ksplit, bn, nstage, kind;
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 6;
+constexpr int kNumConfigs = 7;
 constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
     {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
@@ -36,6 +39,7 @@ constexpr TileCfg kCfg64[kNumConfigs] = {
     {2, 4, 1, 64, 3, 0},   // 3: 256 rows, 4 waves with 64 rows each
     {1, 8, 1, 64, 4, 1},   // 4: ping-pong, 256 rows in two row groups
     {1, 4, 2, 64, 4, 1},   // 5: ping-pong, 128 rows, two key groups
+    {1, 4, 1, 64, 3, 2},   // 6: pipelined, 128 rows, 4 waves
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},
@@ -44,6 +48,7 @@ constexpr TileCfg kCfg128[kNumConfigs] = {
     {2, 4, 1, 64, 3, 0},
     {1, 8, 1, 32, 4, 1},
     {1, 4, 2, 32, 4, 1},
+    {1, 4, 1, 32, 3, 2},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
@@ -110,6 +115,7 @@ hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream
     case 3: return launch_one<D, DT, MASK, 2, 4, 1, 64, 3>(p, grid, stream);
     case 4: return launch_pp<D, DT, MASK, 4, true, small ? 64 : 32>(p, grid, stream);
     case 5: return launch_pp<D, DT, MASK, 4, false, small ? 64 : 32>(p, grid, stream);
+    case 6: return attnfwd::launch_pipelined(D, DT, MASK, cfg, p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -266,7 +272,24 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     p.c = (float)std::min(std::max(cabs, std::ldexp(1.0, -100)), (double)FLT_MAX);
     p.qsign = scale < 0.0f ? 0x80008000u : 0u;
 
-    const hipError_t err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
+    hipError_t err = hipSuccess;
+    if (tc.kind == 2) {
+        // The pipelined kernel has no two-term-P path: the leading query
+        // tiles whose first row sees few keys (a prefix in tile order) run on
+        // the lockstep kernel with the same 128-row tiling, the rest on the
+        // pipelined one (it takes the tiles from the last down, so n_qtiles
+        // keeps its meaning there).  The two launches write disjoint rows.
+        const int64_t n_exact = exact_tiles(N, causal, mask == attnfwd::MASK_WINDOW ? p.window : 0, bm);
+        if (n_exact > 0) {
+            Params pe = p;
+            pe.n_qtiles = (int)n_exact;
+            err = launch(d, dtype, mask, 0, pe, B * Hq * n_exact, (hipStream_t)stream);
+        }
+        if (err == hipSuccess && n_exact < ntiles)
+            err = launch(d, dtype, mask, id, p, B * Hq * (ntiles - n_exact), (hipStream_t)stream);
+    } else {
+        err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
+    }
     if (err == hipErrorNoBinaryForGpu || err == hipErrorInvalidDeviceFunction || err == hipErrorNoDevice ||
         err == hipErrorInvalidDevice)
         return ATTN_ERR_DEVICE;

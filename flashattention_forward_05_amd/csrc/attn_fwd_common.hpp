@@ -128,6 +128,27 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_addr) {
 #pragma clang diagnostic pop
 }
 
+// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (the buffer must be smaller than 4 GiB).
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// acc + (both halves of a packed pair of 16-bit values), one v_dot2 with (1, 1).
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t p, float acc) {
+    if constexpr (DT == 0)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), __builtin_bit_cast(f16x2, 0x3c003c00u), acc,
+                                      false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                               acc, false);
+}
+
 // LDS byte address of a pointer into an LDS object.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
@@ -171,6 +192,11 @@ __device__ __forceinline__ void wait_tiles(int younger) {
 // taken, m is raised when it grows by more than TAU, and O and l are rescaled.
 // On edge tiles a key is visible iff lo <= (key offset from j0 + 8g) <= hi.
 template <int DT, int KB, int CB, bool EXACT>
+__device__ __forceinline__ void online_softmax_full(f32x16 (&s)[KB], f32x16 (&o)[CB], float &m, float &l,
+                                                    u32x4 (&ph)[2 * KB], u32x4 (&pl)[2 * KB], float c,
+                                                    bool edge, int hi, int lo);
+
+template <int DT, int KB, int CB, bool EXACT>
 __device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], f32x16 (&o)[CB], float &m, float &l,
                                                u32x4 (&ph)[2 * KB], u32x4 (&pl)[2 * KB], float c,
                                                bool edge, int hi, int lo) {
@@ -195,6 +221,15 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], f32x16 (&o)[CB],
             }
         }
     }
+    online_softmax_full<DT, KB, CB, EXACT>(s, o, m, l, ph, pl, c, edge, hi, lo);
+}
+
+// The general update: mask (edge tiles), tile max, lazy raise of the running
+// max with the O / l rescale, then p = 2^(s*c - m).
+template <int DT, int KB, int CB, bool EXACT>
+__device__ __forceinline__ void online_softmax_full(f32x16 (&s)[KB], f32x16 (&o)[CB], float &m, float &l,
+                                                    u32x4 (&ph)[2 * KB], u32x4 (&pl)[2 * KB], float c,
+                                                    bool edge, int hi, int lo) {
     if (edge) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)

@@ -88,6 +88,8 @@ CASES = [
     (2, 8, 2, 520, 128, "bf16", True, 200),
     (1, 6, 3, 777, 128, "f16", True, 0),
     (1, 2, 2, 1000, 64, "bf16", False, 0),
+    (1, 4, 2, 1100, 64, "f16", True, 0),
+    (1, 2, 1, 900, 128, "bf16", True, 300),
 ]
 
 
