@@ -31,7 +31,7 @@ struct TileCfg {
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 7;
+constexpr int kNumConfigs = 8;
 constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
     {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
@@ -40,6 +40,7 @@ constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 8, 1, 64, 4, 1},   // 4: ping-pong, 256 rows in two row groups
     {1, 4, 2, 64, 4, 1},   // 5: ping-pong, 128 rows, two key groups
     {1, 4, 1, 64, 3, 2},   // 6: pipelined, 128 rows, 4 waves
+    {1, 2, 2, 64, 2, 0},   // 7: 64 rows, 4 waves (two key groups), two workgroups per CU
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},
@@ -49,6 +50,7 @@ constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 8, 1, 32, 4, 1},
     {1, 4, 2, 32, 4, 1},
     {1, 4, 1, 32, 3, 2},
+    {1, 2, 2, 32, 2, 0},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
@@ -79,14 +81,20 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int ca
     return ATTN_OK;
 }
 
-// Automatic choice (measured on MI355X): d = 128 with at least two 256-row
-// workgroups per compute unit runs 8 query waves of 32 rows; everything else
-// runs 128-row workgroups with two key groups, which keeps two waves per SIMD
-// busy on small grids.
-int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d) {
-    const int64_t wg256 = B * Hq * ((N + 255) / 256);
-    if (d == 128 && wg256 >= 512) return 2;
-    return 1;
+// Automatic choice (measured on MI355X).  d = 128 with at least two 256-row
+// workgroups per compute unit runs 8 query waves of 32 rows (2); other
+// d = 128 shapes run 128-row workgroups with two key groups (1).  For d = 64,
+// 64-row workgroups, two per compute unit (7), win on small grids and on
+// masked runs, where they spread the uneven causal work over twice as many
+// workgroups; larger unmasked grids keep the 128-row workgroups (1).
+int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask) {
+    const int64_t wg128 = B * Hq * ((N + 127) / 128);
+    if (d == 128) {
+        const int64_t wg256 = B * Hq * ((N + 255) / 256);
+        return wg256 >= 512 ? 2 : 1;
+    }
+    if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 7 : 1;
+    return wg128 < 128 ? 7 : 1;
 }
 
 template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
@@ -116,6 +124,7 @@ hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream
     case 4: return launch_pp<D, DT, MASK, 4, true, small ? 64 : 32>(p, grid, stream);
     case 5: return launch_pp<D, DT, MASK, 4, false, small ? 64 : 32>(p, grid, stream);
     case 6: return attnfwd::launch_pipelined(D, DT, MASK, cfg, p, grid, stream);
+    case 7: return launch_one<D, DT, MASK, 1, 2, 2, small ? 64 : 32, 2>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -212,7 +221,7 @@ int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
     const int rc = check_sizes(B, Hq, Hkv, N, d, causal, window, 1.0f, dtype);
     if (rc != ATTN_OK) return rc;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
-    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d);
+    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d, mask_mode(causal, window));
     const TileCfg &tc = tile_cfg(d, id);
     if (cfg) {
         cfg[0] = tc.bm();
@@ -243,7 +252,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
     if (N == 0) return ATTN_OK;
 
-    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d);
+    const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d, mask_mode(causal, window));
     const TileCfg &tc = tile_cfg(d, id);
     const int bm = tc.bm();
     const int64_t ntiles = (N + bm - 1) / bm;
@@ -264,6 +273,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     p.n_qtiles = (int)ntiles;
     p.n_bh = (int)(B * Hq);
     p.exact_below = kExactBelow;
+    // two 64-row workgroups share a compute unit: pair heavy and light tiles
+    p.zigzag = (id == 7) ? 1 : 0;
     // fold |scale| * log2(e) into one multiplier; a negative scale flips the
     // sign of Q instead (exact for 16-bit values).  A zero or vanishing scale
     // is raised to 2^-100: every score then maps to an exponent that rounds
@@ -283,6 +294,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
         if (n_exact > 0) {
             Params pe = p;
             pe.n_qtiles = (int)n_exact;
+            pe.zigzag = 0;
             err = launch(d, dtype, mask, 0, pe, B * Hq * n_exact, (hipStream_t)stream);
         }
         if (err == hipSuccess && n_exact < ntiles)

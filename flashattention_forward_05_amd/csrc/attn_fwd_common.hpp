@@ -40,6 +40,9 @@ struct Params {
     int n_qtiles;        // ceil(N / BM)
     int n_bh;            // B * Hq
     int exact_below;     // a q-tile whose first row sees fewer keys uses two-term P
+    int zigzag;          // masked runs: 1 = ranks 0 .. n/2-1 take the tiles heavy-first and the
+                         // rest light-first (pairs a heavy and a light tile per compute unit
+                         // when two workgroups share one), 0 = heavy-first throughout
     float c;             // |scale| * log2(e), at least 2^-100
     uint32_t qsign;      // 0x80008000 when scale < 0 (flips the sign of Q), else 0
 };
@@ -138,20 +141,18 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, ui
 #pragma clang diagnostic pop
 }
 
-// acc + (both halves of a packed pair of 16-bit values), one v_dot2 with (1, 1).
-template <int DT>
-__device__ __forceinline__ float add_pair(uint32_t p, float acc) {
-    if constexpr (DT == 0)
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), __builtin_bit_cast(f16x2, 0x3c003c00u), acc,
-                                      false);
-    else
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), __builtin_bit_cast(bf16x2, 0x3f803f80u),
-                                               acc, false);
-}
-
 // LDS byte address of a pointer into an LDS object.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
+}
+
+// Query tile of a masked run for dispatch rank `rank` of n tiles: the tiles
+// with the most visible keys (the last ones) go first; with zigzag the second
+// half of the ranks walks back up from the lightest tile.
+__device__ __forceinline__ int masked_qtile(int rank, int n, int zigzag) {
+    const int h = (n + 1) / 2;
+    if (!zigzag || rank < h) return n - 1 - rank;
+    return rank - h;
 }
 
 // Workgroup barrier with no memory-counter waits; the compiler may not move

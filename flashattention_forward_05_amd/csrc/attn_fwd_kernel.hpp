@@ -266,7 +266,7 @@ struct Kernel {
         const int bid = blockIdx.x;
         const int bh = bid % p.n_bh;
         const int rank = bid / p.n_bh;
-        const int qt = (MASK == MASK_NONE) ? rank : (p.n_qtiles - 1 - rank);
+        const int qt = (MASK == MASK_NONE) ? rank : masked_qtile(rank, p.n_qtiles, p.zigzag);
         const int b = bh / p.Hq;
         const int h = bh - b * p.Hq;
         const int hkv = p.Hq / p.group;

@@ -15,9 +15,12 @@
 // online_softmax) never touches O -- so the exponentials run under the MFMAs.
 // On gfx950 a wave's MFMAs overlap well with its own vector instructions,
 // while an MFMA-only wave beside a VALU-only wave on one SIMD overlaps poorly
-// (measured), so the overlap is built inside the wave.  Tiles that need the
-// general update (the first tile of a row, tiles cut by a mask, a running max
-// that must move, two-term P) take the same steps without the interleaving.
+// (measured), so the overlap is built inside the wave.  Iterations whose tile
+// needs the general update (the first tile of a row, tiles cut by a mask or
+// past the key range, and everything after a running max that had to move)
+// take the same steps without the interleaving.  Query tiles whose rows see
+// few keys (two-term P) are not run here: the host sends them to the lockstep
+// kernel of attn_fwd_kernel.hpp.
 //
 // K and V have separate three-stage LDS rings.  Iteration t reads K of tile
 // t+1 and V of tile t-1; after its barrier it issues the loads of K_{t+3}
@@ -78,7 +81,7 @@ struct Pipe {
         float m[QB], l[QB];       // running max (log2 units) and this lane-half's running sum
         f32x16 s[2][KB][QB];      // S^T of tile t (being normalised) and t+1 (being formed)
         u32x4 ph[2][QB][KS];      // 16-bit P^T of tile t-1 (being consumed) and t (being formed)
-        u32x4 pl[2][QB][KS];      // rounding residual of P (two-term P only)
+        u32x4 pl[2][QB][KS];      // unused here (two-term P runs on the lockstep kernel)
     };
 
     // Does any row of this wave see a key of tile a?
@@ -272,9 +275,8 @@ struct Pipe {
 #pragma unroll
             for (int p = pair_begin(i - 1); p < pair_begin(i); ++p) {
                 const int qb = p / (KS * 4), ks = (p / 4) % KS, q = p % 4;
-                const uint32_t pk = pack2<DT>(ex[p][0], ex[p][1]);
-                st.ph[C][qb][ks][q] = pk;
-                rs[qb][q & 1] = add_pair<DT>(pk, rs[qb][q & 1]);
+                st.ph[C][qb][ks][q] = pack2<DT>(ex[p][0], ex[p][1]);
+                rs[qb][q & 1] += ex[p][0] + ex[p][1];
             }
             // p = 2^(s*c - m) against the running max for this step's pairs
 #pragma unroll
@@ -289,9 +291,8 @@ struct Pipe {
 #pragma unroll
         for (int p = pair_begin(NMF - 1); p < NPAIR; ++p) {
             const int qb = p / (KS * 4), ks = (p / 4) % KS, q = p % 4;
-            const uint32_t pk = pack2<DT>(ex[p][0], ex[p][1]);
-            st.ph[C][qb][ks][q] = pk;
-            rs[qb][q & 1] = add_pair<DT>(pk, rs[qb][q & 1]);
+            st.ph[C][qb][ks][q] = pack2<DT>(ex[p][0], ex[p][1]);
+            rs[qb][q & 1] += ex[p][0] + ex[p][1];
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -463,7 +464,7 @@ struct Pipe {
         const int bid = blockIdx.x;
         const int bh = bid % p.n_bh;
         const int rank = bid / p.n_bh;
-        const int qt = (MASK == MASK_NONE) ? rank : (p.n_qtiles - 1 - rank);
+        const int qt = (MASK == MASK_NONE) ? rank : masked_qtile(rank, p.n_qtiles, p.zigzag);
         const int b = bh / p.Hq;
         const int h = bh - b * p.Hq;
         const int hkv = p.Hq / p.group;

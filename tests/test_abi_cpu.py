@@ -79,7 +79,8 @@ def test_plan_reports_tiles():
     assert p["block_m"] * (8192 // p["block_m"]) == 8192
     assert p["grid"] == 4 * 32 * (8192 // p["block_m"])
     assert p["mask_mode"] == 1 and p["exact_tiles"] >= 1
-    assert fa.attn_fwd_plan(1, 1, 1, 100, 64, 0, 0, 0)["exact_tiles"] == 1   # short non-causal rows
+    short = fa.attn_fwd_plan(1, 1, 1, 100, 64, 0, 0, 0)                     # short non-causal rows:
+    assert short["exact_tiles"] == -(-100 // short["block_m"])             # every query tile two-term
     assert fa.attn_fwd_plan(1, 1, 1, 5000, 64, 0, 0, 0)["exact_tiles"] == 0
     assert fa.attn_fwd_plan(1, 32, 1, 32768, 128, 1, 4096, 1)["mask_mode"] == 2
     for d in (64, 128):
@@ -105,3 +106,18 @@ def test_launch_rejects_before_touching_the_gpu():
     with pytest.raises(fa.AttnError) as e:
         fa.attn_fwd_ex(A, 2 * A, 3 * A, 4 * A, None, 1, 1, 1, 8, 64, 0, 0, 0.1, 0, 99, 0)
     assert e.value.status == 4
+
+
+def test_auto_config_choice():
+    """The automatic tile configuration follows the documented rule: 64-row
+    workgroups for d=64 masked runs and small grids, 128-row workgroups for
+    large unmasked d=64 grids, 256-row workgroups for large d=128 grids."""
+    auto = lambda *a: fa.attn_fwd_plan_ex(*a, -1)["config_id"]
+    assert auto(2, 4, 4, 4096, 64, 1, 0, 0) == 7        # lab, causal
+    assert auto(2, 4, 4, 4096, 64, 0, 0, 0) == 1        # lab, full
+    assert auto(2, 4, 4, 1024, 64, 0, 0, 0) == 7        # small grid
+    assert auto(1, 12, 12, 2048, 64, 0, 0, 0) == 1      # stress, full
+    assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 7      # stress, causal
+    assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 2      # GQA prefill
+    assert auto(1, 32, 1, 32768, 128, 1, 4096, 1) == 2  # MQA with window
+    assert auto(1, 2, 2, 512, 128, 1, 0, 1) == 1        # small d=128 grid
