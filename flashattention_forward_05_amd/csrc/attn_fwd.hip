@@ -275,6 +275,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     p.exact_below = kExactBelow;
     // two 64-row workgroups share a compute unit: pair heavy and light tiles
     p.zigzag = (id == 7) ? 1 : 0;
+    p.xcd_kv = (p.group > 1 && (B * Hkv) % 8 == 0) ? 1 : 0;
     // fold |scale| * log2(e) into one multiplier; a negative scale flips the
     // sign of Q instead (exact for 16-bit values).  A zero or vanishing scale
     // is raised to 2^-100: every score then maps to an exponent that rounds

@@ -40,6 +40,7 @@ struct Params {
     int n_qtiles;        // ceil(N / BM)
     int n_bh;            // B * Hq
     int exact_below;     // a q-tile whose first row sees fewer keys uses two-term P
+    int xcd_kv;          // 1 = place all query heads of a K/V head on one XCD (see bh_of)
     int zigzag;          // masked runs: 1 = ranks 0 .. n/2-1 take the tiles heavy-first and the
                          // rest light-first (pairs a heavy and a light tile per compute unit
                          // when two workgroups share one), 0 = heavy-first throughout
@@ -144,6 +145,19 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, ui
 // LDS byte address of a pointer into an LDS object.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
+}
+
+// (batch * query head) handled by workgroup index j (mod n_bh).  Workgroups
+// are dealt to the 8 XCDs round-robin by index, so with xcd_kv the index is
+// permuted to keep every query head of one K/V head on the same XCD, where
+// its K/V tiles then stay in that XCD's L2: j -> XCD j % 8, which owns the
+// K/V heads kvg with kvg % 8 == j % 8.  Needs (number of K/V heads over the
+// batch) % 8 == 0; bh = kvg * group + index within the group.
+__device__ __forceinline__ int bh_of(int j, int n_bh, int group, int xcd_kv) {
+    if (!xcd_kv) return j;
+    const int x = j % 8, r = j / 8;
+    const int kvg = (r / group) * 8 + x;
+    return kvg * group + r % group;
 }
 
 // Query tile of a masked run for dispatch rank `rank` of n tiles: the tiles

@@ -264,7 +264,7 @@ struct Kernel {
         // ---- which (batch*head, query tile) this workgroup owns; for masked
         // runs the heaviest query tiles (most visible keys) are dispatched first.
         const int bid = blockIdx.x;
-        const int bh = bid % p.n_bh;
+        const int bh = bh_of(bid % p.n_bh, p.n_bh, p.group, p.xcd_kv);
         const int rank = bid / p.n_bh;
         const int qt = (MASK == MASK_NONE) ? rank : masked_qtile(rank, p.n_qtiles, p.zigzag);
         const int b = bh / p.Hq;

@@ -462,7 +462,7 @@ struct Pipe {
         // ---- (batch*head, query tile) of this workgroup; masked runs take
         // the heaviest query tiles first
         const int bid = blockIdx.x;
-        const int bh = bid % p.n_bh;
+        const int bh = bh_of(bid % p.n_bh, p.n_bh, p.group, p.xcd_kv);
         const int rank = bid / p.n_bh;
         const int qt = (MASK == MASK_NONE) ? rank : masked_qtile(rank, p.n_qtiles, p.zigzag);
         const int b = bh / p.Hq;
