@@ -76,13 +76,16 @@ WORKLOADS = {
 
 
 def make_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "f16",
-             seed: int = 0, amplitude: float = 1.0):
-    """Seeded host tensors q (B,Hq,N,d), k and v (B,Hkv,N,d) in fp16/bf16."""
+             seed: int = 0, amplitude: float = 1.0, nk: int | None = None):
+    """Seeded host tensors q (B,Hq,N,d), k and v (B,Hkv,Nk,d) in fp16/bf16,
+    with Nk = N unless nk is given (decoding shapes: N new queries against a
+    cached sequence of nk keys)."""
+    Nk = N if nk is None else int(nk)
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     q = torch.randn(B, Hq, N, d, generator=g, dtype=torch.float32)
-    k = torch.randn(B, Hkv, N, d, generator=g, dtype=torch.float32)
-    v = torch.randn(B, Hkv, N, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float32)
     if amplitude != 1.0:
         q, k, v = q * amplitude, k * amplitude, v * amplitude
     tdt = TORCH_DTYPES[dtype]

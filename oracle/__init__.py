@@ -54,6 +54,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_oracle_rows.restype = ctypes.c_int
     lib.attn_oracle_rows.argtypes = [vp, vp, vp, vp, i64, dp, dp, i64, i64, i64, i64, i64,
                                      ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_fwd_qk.restype = ctypes.c_int
+    lib.attn_oracle_fwd_qk.argtypes = [vp, vp, vp, dp, dp, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_rows_qk.restype = ctypes.c_int
+    lib.attn_oracle_rows_qk.argtypes = [vp, vp, vp, vp, i64, dp, dp, i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
     lib.attn_oracle_decode.restype = ctypes.c_double
     lib.attn_oracle_decode.argtypes = [ctypes.c_uint16, ctypes.c_int]
     lib.attn_oracle_max_threads.restype = ctypes.c_int
@@ -82,28 +88,30 @@ def _as_input(x: np.ndarray, dtype: str) -> np.ndarray:
 def _check_shapes(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D (B, H, N, d)")
-    B, Hq, N, d = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+    B, Hq, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
-    Hkv = k.shape[1]
+    Hkv, Nk = k.shape[1], k.shape[2]
     if Hkv < 1 or Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    return B, Hq, Hkv, N, d
+    return B, Hq, Hkv, Nq, Nk, d
 
 
 def oracle_fwd(q, k, v, *, scale: float, causal: bool = False, window: int = 0,
                dtype: str = "f16", lib: ctypes.CDLL | None = None):
-    """Whole forward in fp64.  q (B,Hq,N,d), k/v (B,Hkv,N,d) as uint16 bit
-    patterns (dtype "f16"/"bf16") or float64 ("f64").  Returns (o, lse) as
-    float64 arrays of shapes (B,Hq,N,d) and (B,Hq,N)."""
+    """Whole forward in fp64.  q (B,Hq,Nq,d), k/v (B,Hkv,Nk,d) as uint16 bit
+    patterns (dtype "f16"/"bf16") or float64 ("f64").  With Nq < Nk the
+    queries are the last Nq positions of the sequence (bottom-right causal
+    alignment).  Returns (o, lse) as float64 arrays of shapes (B,Hq,Nq,d) and
+    (B,Hq,Nq)."""
     lib = lib or load_library()
     q, k, v = (_as_input(x, dtype) for x in (q, k, v))
-    B, Hq, Hkv, N, d = _check_shapes(q, k, v)
-    o = np.zeros((B, Hq, N, d), np.float64)
-    lse = np.zeros((B, Hq, N), np.float64)
-    rc = lib.attn_oracle_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                             o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, N, d,
-                             int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
+    o = np.zeros((B, Hq, Nq, d), np.float64)
+    lse = np.zeros((B, Hq, Nq), np.float64)
+    rc = lib.attn_oracle_fwd_qk(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, Nq, Nk, d,
+                                int(bool(causal)), int(window), float(scale), DTYPES[dtype])
     if rc != 0:
         raise RuntimeError(f"attn_oracle_fwd failed with code {rc}")
     return o, lse
@@ -111,18 +119,18 @@ def oracle_fwd(q, k, v, *, scale: float, causal: bool = False, window: int = 0,
 
 def oracle_rows(q, k, v, row_ids, *, scale: float, causal: bool = False, window: int = 0,
                 dtype: str = "f16", lib: ctypes.CDLL | None = None):
-    """Selected rows in fp64.  row_ids are flat (b*Hq + h)*N + i.  Returns
+    """Selected rows in fp64.  row_ids are flat (b*Hq + h)*Nq + i.  Returns
     (o (n, d), lse (n,)) as float64."""
     lib = lib or load_library()
     q, k, v = (_as_input(x, dtype) for x in (q, k, v))
-    B, Hq, Hkv, N, d = _check_shapes(q, k, v)
+    B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
     ids = np.ascontiguousarray(np.asarray(row_ids, dtype=np.int64))
     n = ids.shape[0]
     o = np.zeros((n, d), np.float64)
     lse = np.zeros((n,), np.float64)
-    rc = lib.attn_oracle_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, ids.ctypes.data, n,
-                              o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, N, d,
-                              int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    rc = lib.attn_oracle_rows_qk(q.ctypes.data, k.ctypes.data, v.ctypes.data, ids.ctypes.data, n,
+                                 o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, Nq, Nk, d,
+                                 int(bool(causal)), int(window), float(scale), DTYPES[dtype])
     if rc != 0:
         raise RuntimeError(f"attn_oracle_rows failed with code {rc}")
     return o, lse

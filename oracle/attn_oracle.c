@@ -39,6 +39,13 @@
  *  - A row with no visible key (unreachable through the library's argument
  *    rules) yields o = 0 and lse = -inf, the limit of the all-masked-row guard
  *    in "Lab 02", "Errores tipicos".
+ *  - Fewer queries than keys (Nq < Nk, the decoding case of "Optimizaciones de
+ *    Atencion", section "FlashDecoding": a few new query tokens against a
+ *    cached sequence): the pages do not say how the causal mask aligns.
+ *    Reading taken: the Nq queries are the last Nq positions of the sequence,
+ *    so query row i sits at position Nk - Nq + i and the masks above apply to
+ *    that position (bottom-right alignment).  With Nq = Nk this is the plain
+ *    case.
  *
  * Inputs are the raw bit patterns the GPU receives (fp16 or bf16), decoded
  * exactly to double by the decoders below; a float64 input mode exists for
@@ -112,32 +119,34 @@ int attn_oracle_max_threads(void)
 #endif
 }
 
-/* Visible key range [lo, hi] of query row i (empty when lo > hi). */
-static void visible_range(int64_t i, int64_t N, int causal, int64_t window,
+/* Visible key range [lo, hi] of query row i of Nq against Nk keys (empty
+ * when lo > hi); the row sits at sequence position Nk - Nq + i. */
+static void visible_range(int64_t i, int64_t Nq, int64_t Nk, int causal, int64_t window,
                           int64_t *lo, int64_t *hi)
 {
-    *hi = causal ? i : N - 1;
+    int64_t pos = Nk - Nq + i;
+    *hi = causal ? (pos < Nk - 1 ? pos : Nk - 1) : Nk - 1;
     *lo = 0;
-    if (window > 0 && i - window + 1 > 0)
-        *lo = i - window + 1;
+    if (window > 0 && pos - window + 1 > 0)
+        *lo = pos - window + 1;
 }
 
 /*
  * One output row: o_row[0..d) and *lse_out for (b, h, i).
- * s is scratch for at least N doubles, qrow scratch for d doubles.
+ * s is scratch for at least Nk doubles, qrow scratch for d doubles.
  */
 static void oracle_row(const void *q, const void *k, const void *v,
                        int64_t b, int64_t h, int64_t i,
-                       int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                       int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                        int causal, int64_t window, double scale, int dtype,
                        double *o_row, double *lse_out, double *s, double *qrow)
 {
     int64_t group = Hq / Hkv;
     int64_t hk = h / group;
-    int64_t qbase = ((b * Hq + h) * N + i) * d;
-    int64_t kvhead = (b * Hkv + hk) * N * d;
+    int64_t qbase = ((b * Hq + h) * Nq + i) * d;
+    int64_t kvhead = (b * Hkv + hk) * Nk * d;
     int64_t lo, hi;
-    visible_range(i, N, causal, window, &lo, &hi);
+    visible_range(i, Nq, Nk, causal, window, &lo, &hi);
 
     for (int64_t c = 0; c < d; ++c) {
         o_row[c] = 0.0;
@@ -173,23 +182,24 @@ static void oracle_row(const void *q, const void *k, const void *v,
 }
 
 /*
- * Full forward.  q, o: (B, Hq, N, d); k, v: (B, Hkv, N, d); lse: (B, Hq, N);
- * all row-major.  o and lse are float64.  Returns 0, or -1 on bad arguments,
- * -2 when scratch cannot be allocated.
+ * Full forward, Nq queries against Nk keys.  q, o: (B, Hq, Nq, d); k, v:
+ * (B, Hkv, Nk, d); lse: (B, Hq, Nq); all row-major.  o and lse are float64.
+ * Returns 0, or -1 on bad arguments, -2 when scratch cannot be allocated.
  */
-int attn_oracle_fwd(const void *q, const void *k, const void *v,
-                    double *o, double *lse,
-                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                    int causal, int64_t window, float scale, int dtype)
+int attn_oracle_fwd_qk(const void *q, const void *k, const void *v,
+                       double *o, double *lse,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                       int causal, int64_t window, float scale, int dtype)
 {
-    if (B < 0 || Hq < 1 || Hkv < 1 || N < 0 || d < 1 || Hq % Hkv != 0 ||
+    if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || d < 1 || Hq % Hkv != 0 ||
         window < 0 || dtype < ORACLE_F16 || dtype > ORACLE_F64)
         return -1;
-    int64_t rows = B * Hq * N;
+    int64_t N = Nq;
+    int64_t rows = B * Hq * Nq;
     int failed = 0;
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
         double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
         if (!s || !qrow) {
 #pragma omp atomic write
@@ -200,7 +210,7 @@ int attn_oracle_fwd(const void *q, const void *k, const void *v,
                 int64_t i = r % N;
                 int64_t h = (r / N) % Hq;
                 int64_t b = r / (N * Hq);
-                oracle_row(q, k, v, b, h, i, Hq, Hkv, N, d, causal, window,
+                oracle_row(q, k, v, b, h, i, Hq, Hkv, Nq, Nk, d, causal, window,
                            (double)scale, dtype, o + r * d, lse + r, s, qrow);
             }
         }
@@ -210,27 +220,37 @@ int attn_oracle_fwd(const void *q, const void *k, const void *v,
     return failed ? -2 : 0;
 }
 
+/* Full forward with Nq = Nk = N. */
+int attn_oracle_fwd(const void *q, const void *k, const void *v,
+                    double *o, double *lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    int causal, int64_t window, float scale, int dtype)
+{
+    return attn_oracle_fwd_qk(q, k, v, o, lse, B, Hq, Hkv, N, N, d, causal, window, scale, dtype);
+}
+
 /*
  * Selected rows only, for full-size checks where the whole output would take
- * too long on the CPU.  row_ids[r] is the flat row index (b * Hq + h) * N + i.
+ * too long on the CPU.  row_ids[r] is the flat row index (b * Hq + h) * Nq + i.
  * o: (nrows, d) float64; lse: (nrows,) float64.
  */
-int attn_oracle_rows(const void *q, const void *k, const void *v,
-                     const int64_t *row_ids, int64_t nrows,
-                     double *o, double *lse,
-                     int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                     int causal, int64_t window, float scale, int dtype)
+int attn_oracle_rows_qk(const void *q, const void *k, const void *v,
+                        const int64_t *row_ids, int64_t nrows,
+                        double *o, double *lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                        int causal, int64_t window, float scale, int dtype)
 {
-    if (B < 0 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv != 0 ||
+    if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1 || Hq % Hkv != 0 ||
         window < 0 || dtype < ORACLE_F16 || dtype > ORACLE_F64 || nrows < 0)
         return -1;
+    int64_t N = Nq;
     for (int64_t r = 0; r < nrows; ++r)
         if (row_ids[r] < 0 || row_ids[r] >= B * Hq * N)
             return -1;
     int failed = 0;
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
         double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
         if (!s || !qrow) {
 #pragma omp atomic write
@@ -242,7 +262,7 @@ int attn_oracle_rows(const void *q, const void *k, const void *v,
                 int64_t i = id % N;
                 int64_t h = (id / N) % Hq;
                 int64_t b = id / (N * Hq);
-                oracle_row(q, k, v, b, h, i, Hq, Hkv, N, d, causal, window,
+                oracle_row(q, k, v, b, h, i, Hq, Hkv, Nq, Nk, d, causal, window,
                            (double)scale, dtype, o + r * d, lse + r, s, qrow);
             }
         }
@@ -250,4 +270,15 @@ int attn_oracle_rows(const void *q, const void *k, const void *v,
         free(qrow);
     }
     return failed ? -2 : 0;
+}
+
+/* Selected rows with Nq = Nk = N. */
+int attn_oracle_rows(const void *q, const void *k, const void *v,
+                     const int64_t *row_ids, int64_t nrows,
+                     double *o, double *lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     int causal, int64_t window, float scale, int dtype)
+{
+    return attn_oracle_rows_qk(q, k, v, row_ids, nrows, o, lse, B, Hq, Hkv, N, N, d,
+                               causal, window, scale, dtype);
 }

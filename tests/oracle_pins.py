@@ -361,6 +361,67 @@ def pin_large_scores(lib):
     close(lse[0, 0], [800.0 + math.log1p(w)] * 4, 1e-12, "large-score lse")
 
 
+def pin_decode_is_tail_of_square(lib):
+    """Nq < Nk: the queries are the last Nq positions.  The result must equal
+    the last Nq rows of the square Nk x Nk forward whose last Nq query rows
+    are these queries (every mask, GQA, both dtypes)."""
+    for (B, Hq, Hkv, Nq, Nk, d, dtype, seed) in [(2, 4, 2, 3, 29, 16, "f16", 41),
+                                                 (1, 2, 1, 1, 40, 8, "bf16", 42),
+                                                 (1, 3, 3, 7, 7, 8, "f16", 43)]:
+        qf, k, v = (to_bits(t) for t in make_qkv(B, Hq, Hkv, Nk, d, dtype, seed=seed))
+        q = np.ascontiguousarray(qf[:, :, Nk - Nq:, :])
+        for causal, window in MASKS + [(True, 40)]:
+            o, lse = run(lib, q, k, v, 0.3, causal, window, dtype)
+            of, lf = run(lib, qf, k, v, 0.3, causal, window, dtype)
+            close(o, of[:, :, Nk - Nq:, :], 0.0, f"tail o causal={causal} W={window}")
+            close(lse, lf[:, :, Nk - Nq:], 0.0, f"tail lse causal={causal} W={window}")
+
+
+def pin_decode_brute_force(lib):
+    """Nq < Nk against the definition with exactly rounded sums, and the
+    closed form for zero scores: the mean of the visible V rows (the last
+    min(W, pos + 1) keys of row position pos) with LSE = ln(count)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 3, 11, 8
+    q, k, v = (to_bits(t) for t in make_qkv(B, Hq, Hkv, Nq, d, "f16", seed=44, nk=Nk))
+    qd, kd, vd = (lib_decode(x, "f16") for x in (q, k, v))
+    for causal, window in MASKS:
+        o, lse = run(lib, q, k, v, 0.35, causal, window, "f16")
+        for b in range(B):
+            for h in range(Hq):
+                hk = h // (Hq // Hkv)
+                want_o, want_lse = pyref.batch_attention(qd[b, h].tolist(), kd[b, hk].tolist(),
+                                                         vd[b, hk].tolist(), scale32(0.35), causal, window)
+                close(o[b, h], want_o, 1e-13, f"decode brute o causal={causal} W={window}")
+                close(lse[b, h], want_lse, 1e-13, f"decode brute lse causal={causal} W={window}")
+        oz, lz = run(lib, q, k, v, 0.0, causal, window, "f16")
+        for i in range(Nq):
+            pos = Nk - Nq + i
+            hi = pos if causal else Nk - 1
+            lo = max(0, pos - window + 1) if window > 0 else 0
+            close(oz[0, :, i, :], np.repeat(vd[0], Hq // Hkv, 0)[:, lo:hi + 1, :].mean(axis=1), 1e-14,
+                  "decode zero-score mean")
+            close(lz[0, :, i], [math.log(hi - lo + 1)] * Hq, 1e-14, "decode zero-score lse")
+
+
+def pin_split_kv_merge(lib):
+    """The chunked partial-softmax-and-merge of "Optimizaciones de Atencion",
+    section "FlashDecoding", equals the plain definition for every chunk count
+    (including more chunks than keys, so that some are empty), square and
+    decoding shapes, every mask; and the oracle agrees with both."""
+    for (nq, nk, d, seed) in [(1, 23, 6, 51), (4, 17, 5, 52), (9, 9, 4, 53)]:
+        q, k, v = (to_bits(t) for t in make_qkv(1, 1, 1, nq, d, "bf16", seed=seed, nk=nk))
+        qd, kd, vd = (lib_decode(x, "bf16")[0, 0].tolist() for x in (q, k, v))
+        for causal, window in MASKS:
+            o, lse = run(lib, q, k, v, 0.4, causal, window, "bf16")
+            bo, bl = pyref.batch_attention(qd, kd, vd, scale32(0.4), causal, window)
+            for n_splits in (1, 2, 3, 5, nk, nk + 3):
+                so, sl = pyref.split_kv_attention(qd, kd, vd, scale32(0.4), n_splits, causal, window)
+                close(so, bo, 1e-13, f"split o P={n_splits}")
+                close(sl, bl, 1e-13, f"split lse P={n_splits}")
+                close(o[0, 0], so, 1e-13, f"oracle vs split o P={n_splits}")
+                close(lse[0, 0], sl, 1e-13, f"oracle vs split lse P={n_splits}")
+
+
 ALL_PINS = [
     pin_decoders,
     pin_tiled_demo,
@@ -377,4 +438,7 @@ ALL_PINS = [
     pin_row_entry,
     pin_online_matches_oracle,
     pin_large_scores,
+    pin_decode_is_tail_of_square,
+    pin_decode_brute_force,
+    pin_split_kv_merge,
 ]

@@ -16,10 +16,16 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
 MUTANTS = {
     "scale_dropped": ("s[j - lo] = scale * dot;", "s[j - lo] = dot;"),
-    "causal_excludes_self": ("*hi = causal ? i : N - 1;", "*hi = causal ? i - 1 : N - 1;"),
-    "causal_sees_next": ("*hi = causal ? i : N - 1;", "*hi = causal ? (i + 1 < N ? i + 1 : i) : N - 1;"),
-    "window_one_wider": ("*lo = i - window + 1;", "*lo = i - window;"),
-    "window_condition_off": ("if (window > 0 && i - window + 1 > 0)", "if (window > 0 && i - window > 0)"),
+    "causal_excludes_self": ("*hi = causal ? (pos < Nk - 1 ? pos : Nk - 1) : Nk - 1;",
+                             "*hi = causal ? (pos - 1 < Nk - 1 ? pos - 1 : Nk - 1) : Nk - 1;"),
+    "causal_sees_next": ("*hi = causal ? (pos < Nk - 1 ? pos : Nk - 1) : Nk - 1;",
+                         "*hi = causal ? (pos + 1 < Nk - 1 ? pos + 1 : Nk - 1) : Nk - 1;"),
+    "window_one_wider": ("*lo = pos - window + 1;", "*lo = pos - window;"),
+    "window_condition_off": ("if (window > 0 && pos - window + 1 > 0)", "if (window > 0 && pos - window > 0)"),
+    "decode_top_left": ("int64_t pos = Nk - Nq + i;", "int64_t pos = i;"),
+    "decode_offset_one_short": ("int64_t pos = Nk - Nq + i;", "int64_t pos = Nk - Nq + i - 1;"),
+    "kv_head_stride_uses_nq": ("int64_t kvhead = (b * Hkv + hk) * Nk * d;",
+                               "int64_t kvhead = (b * Hkv + hk) * Nq * d;"),
     "gqa_modulo_map": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
     "k_v_swapped": ("dot += qrow[c] * load_elem(k, dtype, kvhead + j * d + c);",
                     "dot += qrow[c] * load_elem(v, dtype, kvhead + j * d + c);"),
