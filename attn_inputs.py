@@ -35,17 +35,23 @@ class Workload:
     causal: bool
     window: int = 0
     amplitude: float = 1.0
+    Nk: int = 0          # keys per head; 0 means N (N queries are then the last N positions)
     note: str = field(default="", compare=False)
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
+    @property
+    def nk(self) -> int:
+        return self.Nk or self.N
+
     def label(self) -> str:
         mask = "causal" if self.causal else "full"
         if self.window:
             mask += f"_w{self.window}"
-        return (f"{self.name}:B{self.B}_Hq{self.Hq}_Hkv{self.Hkv}_N{self.N}_d{self.d}_"
+        n = f"N{self.N}" if self.nk == self.N else f"Nq{self.N}_Nk{self.nk}"
+        return (f"{self.name}:B{self.B}_Hq{self.Hq}_Hkv{self.Hkv}_{n}_d{self.d}_"
                 f"{self.dtype}_{mask}")
 
 
@@ -72,6 +78,14 @@ WORKLOADS = {
                            note="MQA long context, sliding window 4096"),
     "mqa_causal": Workload("mqa", 1, 32, 1, 32768, 128, "bf16", True,
                            note="MQA long context, full causal"),
+    # decoding ("Optimizaciones de Atencion", section "FlashDecoding"): one new
+    # query token per sequence against the cached K/V of the GQA and MQA shapes
+    "decode_gqa": Workload("decode", 4, 32, 8, 1, 128, "bf16", True, Nk=8192,
+                           note="GQA decode step: 1 query against 8192 cached keys"),
+    "decode_mqa": Workload("decode", 1, 32, 1, 1, 128, "bf16", True, Nk=32768,
+                           note="MQA decode step: 1 query against 32768 cached keys"),
+    "decode_mqa_window": Workload("decode", 1, 32, 1, 1, 128, "bf16", True, window=4096, Nk=32768,
+                                  note="MQA decode step with a 4096-token sliding window"),
 }
 
 
@@ -93,7 +107,8 @@ def make_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "f16",
 
 
 def make_workload(w: Workload, seed: int = 0):
-    return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed, w.amplitude)
+    return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed, w.amplitude,
+                    nk=None if w.nk == w.N else w.nk)
 
 
 def to_bits(t: torch.Tensor) -> np.ndarray:

@@ -11,10 +11,17 @@ Metric: attention-forward TFLOP/s with 4*B*Hq*N^2*d FLOPs per variant, halved
 when causal; a sliding window counts its visible (query, key) pairs instead.
 Inputs are resident in HBM before the timed region starts.
 
+Decoding workloads (``--workload decode``: one query per head against a long
+K/V cache, "Optimizaciones de Atencion", section "FlashDecoding") run the
+split-KV entry point (attention kernel over key chunks, then the merge kernel)
+with a workspace allocated before timing; ``--splitkv`` runs any workload that
+way.  Their FLOPs are 4*d per visible (query, key) pair, and since they move
+far more bytes than they compute on, their roofline is HBM bandwidth.
+
 Prints one JSON line.  Extra fields: "roofline" for the dominant kernel
-(achieved = its FLOPs per launch / its mean launch time from HIP events on the
-launch stream) and "cpu_baseline" (the fp64 oracle on a bounded sample of the
-same workload, on this host's cores).
+(achieved = its FLOPs, or algorithmic bytes, per launch / its mean launch time
+from HIP events on the launch stream) and "cpu_baseline" (the fp64 oracle on a
+bounded sample of the same workload, on this host's cores).
 """
 from __future__ import annotations
 
@@ -30,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}     # MI355X dense fp16/bf16 MFMA, 256 CU x 2.4 GHz x 4096
+PEAK_HBM_GBS = 8000.0                              # MI355X HBM3E
+RIDGE = PEAK_TFLOPS["f16"] * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 WORKLOAD_SETS = {
     "lab": ["lab_n256_full", "lab_n256_causal", "lab_n1024_full", "lab_n1024_causal",
             "lab_n4096_full", "lab_n4096_causal"],
@@ -41,6 +50,9 @@ WORKLOAD_SETS = {
     "lab4096": ["lab_n4096_full", "lab_n4096_causal"],
     "lab_n4096_full": ["lab_n4096_full"],
     "mqa_causal": ["mqa_causal"],
+    "decode": ["decode_gqa", "decode_mqa", "decode_mqa_window"],
+    "decode_gqa": ["decode_gqa"],
+    "decode_mqa": ["decode_mqa"],
 }
 
 
@@ -54,10 +66,32 @@ def metric_flops(B, Hq, N, d, causal, window=0) -> float:
     return f / 2 if causal else f
 
 
-def visible_keys(i, N, causal, window):
-    hi = i if causal else N - 1
-    lo = max(0, i - window + 1) if window > 0 else 0
-    return hi - lo + 1
+def visible_keys(i, N, causal, window, Nk=None):
+    """Keys visible from query row i of N against Nk keys (row i sits at
+    position Nk - N + i)."""
+    Nk = N if Nk is None else Nk
+    pos = Nk - N + i
+    hi = min(pos, Nk - 1) if causal else Nk - 1
+    lo = max(0, pos - window + 1) if window > 0 else 0
+    return max(0, hi - lo + 1)
+
+
+def workload_flops(w) -> float:
+    """The metric's FLOPs for a workload; with Nq != Nk, 4*d per visible pair."""
+    if w.nk == w.N:
+        return metric_flops(w.B, w.Hq, w.N, w.d, w.causal, w.window)
+    pairs = sum(visible_keys(i, w.N, w.causal, w.window, w.nk) for i in range(w.N))
+    return 4.0 * w.B * w.Hq * w.d * pairs
+
+
+def algorithmic_bytes(w) -> float:
+    """Bytes the call must move at least: Q and the K/V rows some query sees
+    (once), O and LSE written."""
+    # the first query row (position nk - N) has the lowest first visible key
+    lo = max(0, w.nk - w.N - w.window + 1) if (w.causal and w.window > 0) else 0
+    kv_rows = (w.nk - lo) if w.N > 0 else 0
+    return (2.0 * w.B * w.Hq * w.N * w.d * 2 + 2.0 * w.B * w.Hkv * kv_rows * w.d * 2
+            + 4.0 * w.B * w.Hq * w.N)
 
 
 def kernel_source_hash() -> str:
@@ -110,7 +144,8 @@ def cpu_baseline(workloads, budget_s: float):
                                window=w.window, dtype=w.dtype)
             t_var += time.perf_counter() - t0
             rows_done += len(chunk)
-            flops += sum(4.0 * w.d * visible_keys(int(r) % w.N, w.N, w.causal, w.window) for r in chunk)
+            flops += sum(4.0 * w.d * visible_keys(int(r) % w.N, w.N, w.causal, w.window, w.nk)
+                         for r in chunk)
             if t_var > per_variant:
                 break
         elapsed += t_var
@@ -191,6 +226,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=-1, help="tile configuration id (-1: automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splitkv", action="store_true",
+                    help="run every variant through the split-KV entry point (decoding workloads always are)")
+    ap.add_argument("--splits", type=int, default=0, help="key chunks for split-KV calls (0: automatic)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a summary of a rocprofv3 kernel-trace CSV dir")
@@ -257,17 +295,31 @@ def main() -> int:
         q, k, v = (t.to(dev) for t in make_workload(w, seed=0))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-        plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
-                                   0 if w.dtype == "f16" else 1, args.config)
-        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan,
-                         flops=metric_flops(w.B, w.Hq, w.N, w.d, w.causal, w.window)))
+        dt = 0 if w.dtype == "f16" else 1
+        split = args.splitkv or w.nk != w.N
+        ws = None
+        if split:
+            plan = fa.attn_fwd_splitkv_plan(w.B, w.Hq, w.Hkv, w.N, w.nk, w.d, w.causal, w.window, dt,
+                                            args.splits, args.config)
+            ws = torch.empty(max(16, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
+        else:
+            plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dt, args.config)
+        flops = workload_flops(w)
+        nbytes = algorithmic_bytes(w)
+        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan, split=split, ws=ws, dt=dt,
+                         flops=flops, bytes=nbytes, hbm_bound=flops / nbytes < RIDGE))
 
     def launch(r):
         # the current stream is torch's capture stream while a graph is recorded
         w = r["w"]
-        fa.attn_fwd_ex(r["q"], r["k"], r["v"], r["o"], r["lse"], w.B, w.Hq, w.Hkv, w.N, w.d,
-                       w.causal, w.window, w.scale, 0 if w.dtype == "f16" else 1, args.config,
-                       torch.cuda.current_stream(dev).cuda_stream)
+        s = torch.cuda.current_stream(dev).cuda_stream
+        if r["split"]:
+            fa.attn_fwd_splitkv_ex(r["q"], r["k"], r["v"], r["o"], r["lse"], w.B, w.Hq, w.Hkv, w.N, w.nk, w.d,
+                                   w.causal, w.window, w.scale, r["dt"], args.splits, args.config, r["ws"],
+                                   r["ws"].numel(), s)
+        else:
+            fa.attn_fwd_ex(r["q"], r["k"], r["v"], r["o"], r["lse"], w.B, w.Hq, w.Hkv, w.N, w.d,
+                           w.causal, w.window, w.scale, r["dt"], args.config, s)
 
     for r in runs:                       # eager warm-up (also checks every launch)
         launch(r)
@@ -322,13 +374,23 @@ def main() -> int:
 
     dom = max(range(len(runs)), key=lambda j: per_kernel_ms[j])
     dw = runs[dom]["w"]
-    achieved = runs[dom]["flops"] / (per_kernel_ms[dom] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dw.dtype]
+    if runs[dom]["hbm_bound"]:
+        # decoding: the call (attention over key chunks + merge) against HBM bandwidth
+        roof = {"bound": "hbm", "achieved": runs[dom]["bytes"] / (per_kernel_ms[dom] * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "algorithmic_bytes": runs[dom]["bytes"]}
+    else:
+        roof = {"bound": "mfma", "achieved": runs[dom]["flops"] / (per_kernel_ms[dom] * 1e-3) / 1e12,
+                "peak": peak, "unit": "TFLOP/s"}
     kernels = []
     for j, r in enumerate(runs):
+        t = per_kernel_ms[j] * 1e-3
         kernels.append({"variant": r["w"].label(), "ms": round(per_kernel_ms[j], 5),
-                        "tflops": round(r["flops"] / (per_kernel_ms[j] * 1e-3) / 1e12, 2),
-                        "frac_of_peak": round(r["flops"] / (per_kernel_ms[j] * 1e-3) / 1e12 / peak, 4),
+                        "tflops": round(r["flops"] / t / 1e12, 2),
+                        "frac_of_peak": round(r["flops"] / t / 1e12 / peak, 4),
+                        "hbm_gbs": round(r["bytes"] / t / 1e9, 1),
+                        "frac_of_hbm": round(r["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
+                        "split_kv": r["split"],
                         "plan": r["plan"]})
 
     result = {
@@ -349,15 +411,17 @@ def main() -> int:
             "variants": [w.label() for w in wls],
             "parallelism": "single GPU",
             "tile_config": args.config,
+            "split_kv": any(r["split"] for r in runs),
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": roof["bound"],
             "kernel": dw.label(),
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            "achieved": round(roof["achieved"], 2),
+            "peak": roof["peak"],
+            "unit": roof["unit"],
+            "frac": round(roof["achieved"] / roof["peak"], 4),
             "traffic": traffic_from_profiles(dw.label()),
+            **({"algorithmic_bytes": roof["algorithmic_bytes"]} if "algorithmic_bytes" in roof else {}),
         },
         "kernels": kernels,
         "frac_of_peak_whole_step": round(value / PEAK_TFLOPS[wls[0].dtype], 4),

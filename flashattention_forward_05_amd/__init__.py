@@ -12,6 +12,12 @@ Entry points (same names as the C ABI): ``attn_fwd``, ``attn_fwd_ex``,
 the pages' convenience form ``flash_attn_forward(q, k, v, causal=True)``
 ("Lab 02 - Forward de flash attention en Triton", "Bloque A"), which also
 returns the per-row log-sum-exp.
+
+Split-KV ("Optimizaciones de Atencion", section "FlashDecoding"):
+``attn_fwd_splitkv``, ``attn_fwd_splitkv_ex``, ``attn_fwd_splitkv_validate``,
+``attn_fwd_splitkv_plan``, ``attn_fwd_splitkv_workspace_size`` and the
+convenience ``flash_attn_forward_splitkv(q, k, v, causal=True)`` for Nq
+queries against Nk keys (decoding).
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
@@ -24,9 +30,15 @@ from ._binding import (  # noqa: F401
     attn_fwd_num_configs,
     attn_fwd_plan,
     attn_fwd_plan_ex,
+    attn_fwd_splitkv,
+    attn_fwd_splitkv_ex,
+    attn_fwd_splitkv_plan,
+    attn_fwd_splitkv_validate,
+    attn_fwd_splitkv_workspace_size,
     attn_fwd_validate,
     attn_status_str,
     flash_attn_forward,
+    flash_attn_forward_splitkv,
     library_path,
     load_library,
 )

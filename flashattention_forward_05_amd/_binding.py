@@ -13,7 +13,7 @@ ATTN_BF16 = 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_ARG", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_LAUNCH",
-    8: "ATTN_ERR_DEVICE",
+    8: "ATTN_ERR_DEVICE", 9: "ATTN_ERR_WORKSPACE",
 }
 
 _lib = None
@@ -59,6 +59,17 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_num_configs.restype = cint
     lib.attn_fwd_config_desc.argtypes = [cint, i64, i64p]
     lib.attn_fwd_config_desc.restype = cint
+    kv = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, cint, i64, f32, cint, i64]
+    lib.attn_fwd_splitkv.argtypes = kv + [vp, i64, vp]
+    lib.attn_fwd_splitkv.restype = cint
+    lib.attn_fwd_splitkv_ex.argtypes = kv + [cint, vp, i64, vp]
+    lib.attn_fwd_splitkv_ex.restype = cint
+    lib.attn_fwd_splitkv_validate.argtypes = kv + [cint, vp, i64]
+    lib.attn_fwd_splitkv_validate.restype = cint
+    lib.attn_fwd_splitkv_plan.argtypes = [i64, i64, i64, i64, i64, i64, cint, i64, cint, i64, cint, i64p]
+    lib.attn_fwd_splitkv_plan.restype = cint
+    lib.attn_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, cint, i64, cint, i64, cint]
+    lib.attn_fwd_splitkv_workspace_size.restype = i64
     _lib = lib
     return lib
 
@@ -171,4 +182,98 @@ def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: flo
     with torch.cuda.device(q.device):
         attn_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, config_id,
                     torch.cuda.current_stream(q.device).cuda_stream)
+    return out, lse
+
+
+# ---- split-KV ("FlashDecoding"): Nq queries against Nk keys, keys cut into
+# chunks over workgroups and merged by a second kernel
+
+def attn_fwd_splitkv_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                              num_splits=0, config_id=-1, workspace=None, workspace_bytes=0) -> int:
+    """Host-side argument checks of the split-KV call only; returns the status."""
+    return load_library().attn_fwd_splitkv_validate(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal), window, scale,
+        dtype, num_splits, config_id, _ptr(workspace), workspace_bytes)
+
+
+def attn_fwd_splitkv_plan(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits=0, config_id=-1) -> dict:
+    out = (ctypes.c_int64 * 9)()
+    rc = load_library().attn_fwd_splitkv_plan(B, Hq, Hkv, Nq, Nk, d, int(causal), window, dtype,
+                                              num_splits, config_id, out)
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_splitkv_plan")
+    keys = ("block_m", "block_n", "waves", "grid", "n_splits", "split_tiles", "config_id", "workspace_bytes",
+            "stacked")
+    return dict(zip(keys, list(out)))
+
+
+def attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits=0,
+                                    config_id=-1) -> int:
+    n = int(load_library().attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(causal), window,
+                                                           dtype, num_splits, config_id))
+    if n < 0:
+        raise AttnError(-n, "attn_fwd_splitkv_workspace_size")
+    return n
+
+
+def attn_fwd_splitkv_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                        num_splits=0, config_id=-1, workspace=None, workspace_bytes=0, stream=None) -> None:
+    """Enqueue the split-KV forward; raises AttnError."""
+    rc = load_library().attn_fwd_splitkv_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal), window, scale,
+        dtype, num_splits, config_id, _ptr(workspace), workspace_bytes, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_splitkv_ex")
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                     num_splits=0, workspace=None, workspace_bytes=0, stream=None) -> None:
+    """Enqueue the split-KV forward with the automatic tile choice."""
+    rc = load_library().attn_fwd_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal), window, scale,
+        dtype, num_splits, _ptr(workspace), workspace_bytes, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_splitkv")
+
+
+def flash_attn_forward_splitkv(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None,
+                               num_splits: int = 0, config_id: int = -1, workspace=None, out=None, lse=None,
+                               return_lse: bool = True):
+    """(B, Hq, Nq, d) query against (B, Hkv, Nk, d) key/value fp16 or bf16
+    CUDA tensors -> (o, lse), the queries being the last Nq positions.  The
+    workspace (a CUDA uint8 tensor of at least attn_fwd_splitkv_workspace_size
+    bytes) is allocated with torch when not given."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (B, H, N, d), got shape {tuple(t.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
+    B, Hq, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dtype = ATTN_F16 if q.dtype == torch.float16 else ATTN_BF16
+    need = attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits, config_id)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        attn_fwd_splitkv_ex(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                            num_splits, config_id, workspace, ws_bytes,
+                            torch.cuda.current_stream(q.device).cuda_stream)
     return out, lse

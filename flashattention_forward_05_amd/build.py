@@ -13,14 +13,15 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattn_fwd.so")
 # (source, extra flags): the pipelined kernels keep MFMA results in VGPRs
 SOURCES = [
-    (os.path.join(CSRC, "attn_fwd.hip"), []),
+    (os.path.join(CSRC, "attn_fwd.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_pipe.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Rpass-analysis=kernel-resource-usage"]),
 ]
 # Kernels whose loads are tracked by explicit vmcnt waits must not touch
 # scratch memory (a spill reload would count as an outstanding load).
-NO_SCRATCH = ("attn_fwd_pipe_kernel",)
+NO_SCRATCH = ("attn_fwd_pipe_kernel", "attn_fwd_kernel", "attn_fwd_pingpong_kernel")
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp", "attn_fwd_pingpong.hpp",
-                                            "attn_fwd_pipe.hpp", "attn_fwd_launch.hpp")] + [
+                                            "attn_fwd_pipe.hpp", "attn_fwd_launch.hpp",
+                                            "attn_fwd_merge.hpp")] + [
     os.path.join(INCLUDE, "attn_fwd.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

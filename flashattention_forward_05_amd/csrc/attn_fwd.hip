@@ -11,6 +11,7 @@
 #include "attn_fwd.h"
 #include "attn_fwd_kernel.hpp"
 #include "attn_fwd_launch.hpp"
+#include "attn_fwd_merge.hpp"
 #include "attn_fwd_pingpong.hpp"
 
 namespace {
@@ -31,7 +32,7 @@ struct TileCfg {
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 8;
+constexpr int kNumConfigs = 9;
 constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
     {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
@@ -41,23 +42,29 @@ constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 2, 64, 4, 1},   // 5: ping-pong, 128 rows, two key groups
     {1, 4, 1, 64, 3, 2},   // 6: pipelined, 128 rows, 4 waves
     {1, 2, 2, 64, 2, 0},   // 7: 64 rows, 4 waves (two key groups), two workgroups per CU
+    {1, 1, 1, 64, 3, 0},   // 8: 32 rows, 1 wave (few query rows: decoding)
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},
     {1, 4, 2, 64, 2, 0},
     {1, 8, 1, 64, 3, 0},
-    {2, 4, 1, 64, 3, 0},
+    {2, 4, 1, 32, 3, 0},
     {1, 8, 1, 32, 4, 1},
     {1, 4, 2, 32, 4, 1},
     {1, 4, 1, 32, 3, 2},
     {1, 2, 2, 32, 2, 0},
+    {1, 1, 1, 32, 3, 0},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
+
+// Configurations not built for a head dim (the ping-pong kernel at d = 128).
+bool cfg_built(int64_t d, int id) { return !(d == 128 && tile_cfg(d, id).kind == 1); }
 
 // Query tiles whose first row sees fewer keys than this use the two-term P.
 constexpr int kExactBelow = 256;
 
 constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxSplits = 1024;
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
 
 bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
@@ -120,11 +127,18 @@ hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream
     case 0: return launch_one<D, DT, MASK, 1, 4, 1, 64, 3>(p, grid, stream);
     case 1: return launch_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2>(p, grid, stream);
     case 2: return launch_one<D, DT, MASK, 1, 8, 1, 64, 3>(p, grid, stream);
-    case 3: return launch_one<D, DT, MASK, 2, 4, 1, 64, 3>(p, grid, stream);
-    case 4: return launch_pp<D, DT, MASK, 4, true, small ? 64 : 32>(p, grid, stream);
-    case 5: return launch_pp<D, DT, MASK, 4, false, small ? 64 : 32>(p, grid, stream);
+    case 3: return launch_one<D, DT, MASK, 2, 4, 1, small ? 64 : 32, 3>(p, grid, stream);
+    // the ping-pong kernel is built for d = 64 only: at d = 128 it does not
+    // fit its registers without spilling
+    case 4:
+        if constexpr (small) return launch_pp<D, DT, MASK, 4, true, 64>(p, grid, stream);
+        else return hipErrorInvalidValue;
+    case 5:
+        if constexpr (small) return launch_pp<D, DT, MASK, 4, false, 64>(p, grid, stream);
+        else return hipErrorInvalidValue;
     case 6: return attnfwd::launch_pipelined(D, DT, MASK, cfg, p, grid, stream);
     case 7: return launch_one<D, DT, MASK, 1, 2, 2, small ? 64 : 32, 2>(p, grid, stream);
+    case 8: return launch_one<D, DT, MASK, 1, 1, 1, small ? 64 : 32, 3>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -161,6 +175,142 @@ int64_t exact_tiles(int64_t N, int causal, int64_t window, int bm) {
     return n;
 }
 
+// The merge kernel: groups of D/4 lanes, 256 / (D/4) per workgroup; sg of
+// them (the largest power of two <= min(chunks, groups)) share a row.
+template <int D, int DT>
+hipError_t launch_merge_t(const attnfwd::MergeParams &mp, hipStream_t stream) {
+    constexpr int G = 256 / (D / 4);
+    attnfwd::MergeParams args = mp;
+    args.sg = 1;
+    while (args.sg * 2 <= std::min(G, mp.n_splits)) args.sg *= 2;
+    const int64_t rows_per_block = G / args.sg;
+    void *argv[] = {&args};
+    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_merge_kernel<D, DT>,
+                           dim3((unsigned)((mp.rows + rows_per_block - 1) / rows_per_block)), dim3(256), argv, 0,
+                           stream);
+}
+
+hipError_t launch_merge(int64_t d, int dtype, const attnfwd::MergeParams &mp, hipStream_t stream) {
+    if (d == 64)
+        return dtype == ATTN_F16 ? launch_merge_t<64, 0>(mp, stream) : launch_merge_t<64, 1>(mp, stream);
+    return dtype == ATTN_F16 ? launch_merge_t<128, 0>(mp, stream) : launch_merge_t<128, 1>(mp, stream);
+}
+
+int status_of(hipError_t err) {
+    if (err == hipErrorNoBinaryForGpu || err == hipErrorInvalidDeviceFunction || err == hipErrorNoDevice ||
+        err == hipErrorInvalidDevice)
+        return ATTN_ERR_DEVICE;
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+// Kernel parameters shared by the plain and the split-KV entry points.
+Params make_params(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                   int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t window, int mask, float scale,
+                   int64_t ntiles) {
+    Params p;
+    p.q = (const uint16_t *)q;
+    p.k = (const uint16_t *)k;
+    p.v = (const uint16_t *)v;
+    p.o = (uint16_t *)o;
+    p.lse = lse;
+    p.Hq = (int)Hq;
+    p.N = (int)Nq;
+    p.Nk = (int)Nk;
+    p.q_off = (int)(Nk - Nq);
+    p.pack_nq = 0;
+    p.n_splits = 1;
+    p.split_tiles = INT_MAX / 2;
+    p.split_t0 = 0;
+    p.ws_o = nullptr;
+    p.ws_ml = nullptr;
+    p.group = (int)(Hq / Hkv);
+    p.window = mask == attnfwd::MASK_WINDOW ? (int)std::min<int64_t>(window, Nk) : 0;
+    p.n_qtiles = (int)ntiles;
+    p.n_bh = (int)(B * Hq);
+    p.exact_below = kExactBelow;
+    p.zigzag = 0;
+    p.xcd_kv = (p.group > 1 && (B * Hkv) % 8 == 0) ? 1 : 0;
+    // fold |scale| * log2(e) into one multiplier; a negative scale flips the
+    // sign of Q instead (exact for 16-bit values).  A zero or vanishing scale
+    // is raised to 2^-100: every score then maps to an exponent that rounds
+    // to 0 in fp32, exactly what scale = 0 gives.
+    const double cabs = std::fabs((double)scale) * 1.4426950408889634;
+    p.c = (float)std::min(std::max(cabs, std::ldexp(1.0, -100)), (double)FLT_MAX);
+    p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+    return p;
+}
+
+// ---- split-KV ("FlashDecoding"): Nq queries against Nk keys, the key range
+// cut into chunks over workgroups, partial results merged by a second kernel.
+
+int check_sizes_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                   int64_t window, float scale, int dtype) {
+    if (Nk < 0 || Nk > kMaxN || (Nq > 0 && Nk == 0)) return ATTN_ERR_SHAPE;
+    if (causal && Nq > Nk) return ATTN_ERR_SHAPE;
+    return check_sizes(B, Hq, Hkv, Nq, d, causal, window, scale, dtype);
+}
+
+// Stacked heads: with few query rows (decoding) and G > 1, the G query heads
+// of one K/V head are processed as one head of G * Nq rows, so that each K/V
+// tile is brought on chip once for all of them.  Because q and o are
+// (B, Hq, Nq, d) with the G heads of a K/V group adjacent, those rows are
+// already contiguous: the kernel only needs to know that row r sits at
+// position Nk - Nq + r % Nq.
+constexpr int64_t kStackMaxNq = 16;
+
+struct KvView {
+    int64_t Hq, Nq;   // heads and rows per head as launched
+    int pack_nq;      // 0, or Nq when the heads are stacked
+};
+
+KvView kv_view(int64_t Hq, int64_t Hkv, int64_t Nq) {
+    const int64_t G = Hq / Hkv;
+    if (G > 1 && Nq > 0 && Nq <= kStackMaxNq) return {Hkv, G * Nq, (int)Nq};
+    return {Hq, Nq, 0};
+}
+
+// Automatic choice for split-KV calls: one-wave 32-row workgroups for a few
+// query rows per (stacked) head (decoding), else the choice of the plain
+// forward.
+int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask) {
+    if (Nq <= 32) return 8;
+    return auto_config(B, Hq, Nq, d, mask);
+}
+
+struct SplitPlan {
+    int64_t ntiles, grid, n_splits, split_tiles, t0, ws_bytes;
+};
+
+// Chunks of whole K/V tiles over the tiles some query row sees (with a
+// window, the first row's window start bounds them below).  num_splits = 0
+// picks, from measurement: for a few rows per (stacked) head, enough chunks
+// for about 512 workgroups with at least four tiles each; for longer query
+// blocks no split unless the grid has fewer than 64 workgroups (the partial
+// results and the merge cost more than they save on larger grids).  The
+// count used is ceil(visible tiles / tiles per chunk), so no chunk is empty
+// for every row.
+SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t q_first, int causal, int64_t window,
+                     int64_t d, int64_t num_splits, int id) {
+    SplitPlan sp;
+    const TileCfg &tc = tile_cfg(d, id);
+    sp.ntiles = (Nq + tc.bm() - 1) / tc.bm();
+    const int64_t lo = (causal && window > 0) ? std::max<int64_t>(0, q_first - window + 1) : 0;
+    sp.t0 = lo / tc.bn;
+    const int64_t n_kt = std::max<int64_t>(1, (Nk + tc.bn - 1) / tc.bn - sp.t0);
+    int64_t want = num_splits;
+    if (want == 0) {
+        const int64_t wgs = std::max<int64_t>(1, B * Hq * sp.ntiles);
+        const int64_t target = Nq <= 32 ? 512 : (wgs < 64 ? 128 : 1);
+        want = std::min<int64_t>((target + wgs - 1) / wgs, std::max<int64_t>(1, n_kt / 4));
+    }
+    want = std::max<int64_t>(1, std::min(want, n_kt));
+    sp.split_tiles = (n_kt + want - 1) / want;
+    sp.n_splits = (n_kt + sp.split_tiles - 1) / sp.split_tiles;
+    sp.grid = B * Hq * sp.ntiles * sp.n_splits;
+    sp.ws_bytes = sp.n_splits > 1 ? sp.n_splits * B * Hq * Nq * (d + 1) * 4 : 0;
+    return sp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +326,7 @@ const char *attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "output overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_DEVICE: return "no usable gfx950 device";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_fwd_splitkv_workspace_size";
     default: return "unknown status";
     }
 }
@@ -206,6 +357,7 @@ int attn_fwd_num_configs(void) { return kNumConfigs; }
 
 int attn_fwd_config_desc(int id, int64_t d, int64_t *desc) {
     if (id < 0 || id >= kNumConfigs || !desc || (d != 64 && d != 128)) return ATTN_ERR_ARG;
+    if (!cfg_built(d, id)) return ATTN_ERR_UNSUPPORTED;
     const TileCfg &tc = tile_cfg(d, id);
     desc[0] = tc.qb;
     desc[1] = tc.waves();
@@ -221,6 +373,7 @@ int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
     const int rc = check_sizes(B, Hq, Hkv, N, d, causal, window, 1.0f, dtype);
     if (rc != ATTN_OK) return rc;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    if (config_id >= 0 && !cfg_built(d, config_id)) return ATTN_ERR_UNSUPPORTED;
     const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d, mask_mode(causal, window));
     const TileCfg &tc = tile_cfg(d, id);
     if (cfg) {
@@ -250,6 +403,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     int rc = attn_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype);
     if (rc != ATTN_OK) return rc;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    if (config_id >= 0 && !cfg_built(d, config_id)) return ATTN_ERR_UNSUPPORTED;
     if (N == 0) return ATTN_OK;
 
     const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d, mask_mode(causal, window));
@@ -259,30 +413,10 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     const int64_t grid = B * Hq * ntiles;
     if (grid > INT_MAX) return ATTN_ERR_SHAPE;
 
-    Params p;
-    p.q = (const uint16_t *)q;
-    p.k = (const uint16_t *)k;
-    p.v = (const uint16_t *)v;
-    p.o = (uint16_t *)o;
-    p.lse = lse;
-    p.Hq = (int)Hq;
-    p.N = (int)N;
-    p.group = (int)(Hq / Hkv);
     const int mask = mask_mode(causal, window);
-    p.window = mask == attnfwd::MASK_WINDOW ? (int)std::min<int64_t>(window, N) : 0;
-    p.n_qtiles = (int)ntiles;
-    p.n_bh = (int)(B * Hq);
-    p.exact_below = kExactBelow;
+    Params p = make_params(q, k, v, o, lse, B, Hq, Hkv, N, N, window, mask, scale, ntiles);
     // two 64-row workgroups share a compute unit: pair heavy and light tiles
     p.zigzag = (id == 7) ? 1 : 0;
-    p.xcd_kv = (p.group > 1 && (B * Hkv) % 8 == 0) ? 1 : 0;
-    // fold |scale| * log2(e) into one multiplier; a negative scale flips the
-    // sign of Q instead (exact for 16-bit values).  A zero or vanishing scale
-    // is raised to 2^-100: every score then maps to an exponent that rounds
-    // to 0 in fp32, exactly what scale = 0 gives.
-    const double cabs = std::fabs((double)scale) * 1.4426950408889634;
-    p.c = (float)std::min(std::max(cabs, std::ldexp(1.0, -100)), (double)FLT_MAX);
-    p.qsign = scale < 0.0f ? 0x80008000u : 0u;
 
     hipError_t err = hipSuccess;
     if (tc.kind == 2) {
@@ -303,16 +437,137 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     } else {
         err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
     }
-    if (err == hipErrorNoBinaryForGpu || err == hipErrorInvalidDeviceFunction || err == hipErrorNoDevice ||
-        err == hipErrorInvalidDevice)
-        return ATTN_ERR_DEVICE;
-    return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return status_of(err);
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
              int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, int64_t window, float scale,
              int dtype, void *stream) {
     return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, -1, stream);
+}
+
+int attn_fwd_splitkv_validate(const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                              int64_t Nk, int64_t d, int causal, int64_t window, float scale, int dtype,
+                              int64_t num_splits, int config_id, const void *workspace,
+                              int64_t workspace_bytes) {
+    if (Nq > 0 && (!q || !k || !v || !o)) return ATTN_ERR_NULL;
+    const int rc = check_sizes_kv(B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+    if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    const KvView kv = kv_view(Hq, Hkv, Nq);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
+    if (tile_cfg(d, id).kind != 0) return ATTN_ERR_UNSUPPORTED;
+    const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)workspace;
+    if ((mis & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_ALIGN;
+    if (Nq == 0) return ATTN_OK;
+    const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, Nk, Nk - Nq, causal, window, d, num_splits, id);
+    if (sp.grid > INT_MAX) return ATTN_ERR_SHAPE;
+    if (sp.n_splits > 1 && B * Hq * Nq > INT_MAX) return ATTN_ERR_SHAPE;   // merge grid
+    if (sp.n_splits > 1) {
+        if (!workspace) return ATTN_ERR_NULL;
+        if (workspace_bytes < sp.ws_bytes) return ATTN_ERR_WORKSPACE;
+    }
+    const int64_t qbytes = B * Hq * Nq * d * 2;
+    const int64_t kvbytes = B * Hkv * Nk * d * 2;
+    const int64_t lbytes = B * Hq * Nq * 4;
+    if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k, kvbytes) ||
+        ranges_overlap(o, qbytes, v, kvbytes))
+        return ATTN_ERR_ALIAS;
+    if (lse && (ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
+                ranges_overlap(lse, lbytes, v, kvbytes) || ranges_overlap(lse, lbytes, o, qbytes)))
+        return ATTN_ERR_ALIAS;
+    if (sp.n_splits > 1) {
+        const void *bufs[5] = {q, k, v, o, lse};
+        const int64_t sizes[5] = {qbytes, kvbytes, kvbytes, qbytes, lse ? lbytes : 0};
+        for (int i = 0; i < 5; ++i)
+            if (sizes[i] > 0 && ranges_overlap(workspace, sp.ws_bytes, bufs[i], sizes[i])) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+int attn_fwd_splitkv_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                          int causal, int64_t window, int dtype, int64_t num_splits, int config_id,
+                          int64_t *plan) {
+    const int rc = check_sizes_kv(B, Hq, Hkv, Nq, Nk, d, causal, window, 1.0f, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+    if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    const KvView kv = kv_view(Hq, Hkv, Nq);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
+    const TileCfg &tc = tile_cfg(d, id);
+    if (tc.kind != 0) return ATTN_ERR_UNSUPPORTED;
+    const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, Nk, Nk - Nq, causal, window, d, num_splits, id);
+    if (plan) {
+        plan[0] = tc.bm();
+        plan[1] = tc.bn;
+        plan[2] = tc.waves();
+        plan[3] = Nq > 0 ? sp.grid : 0;
+        plan[4] = sp.n_splits;
+        plan[5] = sp.split_tiles;
+        plan[6] = id;
+        plan[7] = Nq > 0 ? sp.ws_bytes : 0;
+        plan[8] = kv.pack_nq > 0 ? 1 : 0;
+    }
+    return ATTN_OK;
+}
+
+int64_t attn_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                        int64_t d, int causal, int64_t window, int dtype,
+                                        int64_t num_splits, int config_id) {
+    int64_t plan[9];
+    const int rc = attn_fwd_splitkv_plan(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits,
+                                         config_id, plan);
+    return rc == ATTN_OK ? plan[7] : -(int64_t)rc;
+}
+
+int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                        int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        int64_t window, float scale, int dtype, int64_t num_splits, int config_id,
+                        void *workspace, int64_t workspace_bytes, void *stream) {
+    const int rc = attn_fwd_splitkv_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale,
+                                             dtype, num_splits, config_id, workspace, workspace_bytes);
+    if (rc != ATTN_OK) return rc;
+    if (Nq == 0) return ATTN_OK;
+    const int mask = mask_mode(causal, window);
+    const KvView kv = kv_view(Hq, Hkv, Nq);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask);
+    const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, Nk, Nk - Nq, causal, window, d, num_splits, id);
+    // stacked heads: B * Hkv heads of G * Nq rows, each its own K/V head
+    Params p = make_params(q, k, v, o, lse, B, kv.Hq, kv.pack_nq > 0 ? kv.Hq : Hkv, kv.Nq, Nk, window, mask,
+                           scale, sp.ntiles);
+    p.q_off = (int)(Nk - Nq);
+    p.pack_nq = kv.pack_nq;
+    p.zigzag = (id == 7) ? 1 : 0;
+    p.n_splits = (int)sp.n_splits;
+    p.split_tiles = (int)sp.split_tiles;
+    p.split_t0 = (int)sp.t0;
+    const int64_t rows = B * Hq * Nq;
+    if (sp.n_splits > 1) {
+        p.ws_o = (float *)workspace;
+        p.ws_ml = (float *)workspace + sp.n_splits * rows * d;
+    }
+    hipError_t err = launch(d, dtype, mask, id, p, sp.grid, (hipStream_t)stream);
+    if (err == hipSuccess && sp.n_splits > 1) {
+        attnfwd::MergeParams mp;
+        mp.ws_o = p.ws_o;
+        mp.ws_ml = p.ws_ml;
+        mp.o = (uint16_t *)o;
+        mp.lse = lse;
+        mp.rows = rows;
+        mp.n_splits = (int)sp.n_splits;
+        err = launch_merge(d, dtype, mp, (hipStream_t)stream);
+    }
+    return status_of(err);
+}
+
+int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                     int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int causal, int64_t window,
+                     float scale, int dtype, int64_t num_splits, void *workspace, int64_t workspace_bytes,
+                     void *stream) {
+    return attn_fwd_splitkv_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                               num_splits, -1, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -34,7 +34,16 @@ struct Params {
     uint16_t *o;
     float *lse;          // may be null
     int Hq;
-    int N;
+    int N;               // query rows per head
+    int Nk;              // keys per head (= N except for the split-KV entry point)
+    int q_off;           // Nk - N: query row i sits at sequence position i + q_off
+    int pack_nq;         // > 0: a "head" is one K/V head's G query heads stacked (G * pack_nq
+                         // rows); row r then sits at position q_off + r % pack_nq
+    int n_splits;        // key splits over workgroups (1 = none; lockstep kernel only)
+    int split_tiles;     // key tiles per split
+    int split_t0;        // first key tile of split 0 (the first tile any query row sees)
+    float *ws_o;         // n_splits > 1: partial outputs (n_splits, B*Hq, N, d), O/l in fp32
+    float *ws_ml;        // n_splits > 1: partial log2-sum-exp (n_splits, B*Hq, N), m + log2 l
     int group;           // Hq / Hkv
     int window;          // > 0 only with MASK_WINDOW
     int n_qtiles;        // ceil(N / BM)

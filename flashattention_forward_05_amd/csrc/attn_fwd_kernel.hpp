@@ -81,14 +81,36 @@ struct Kernel {
         float lsum[QB];
     };
 
+    // Nq / Nk: query rows and keys; qw0: first query row of the wave; pw0 and
+    // w_last: lowest and highest sequence position of the wave's valid rows
+    // (row + q_off, or q_off + row % pack_nq for stacked heads), and lpos the
+    // position of this lane's rows: what the masks compare keys against.
     struct Ctx {
         const uint16_t *kp, *vp;
-        int N, window, lane, g, l32, wave_q, kgroup;
-        int qw0, w_last;
+        int Nq, Nk, window, lane, g, l32, wave_q, kgroup;
+        int qw0, pw0, w_last;
+        int lpos[QB];
         float c;
         char *kst[NSTAGE];
         char *vst[NSTAGE];
     };
+
+    // Sequence position of query row r, and the lowest / highest position
+    // over rows a .. b (a <= b): with stacked heads the rows of one range can
+    // wrap from one query head to the next.
+    static __device__ __forceinline__ int pos_of(const Params &p, int r) {
+        return p.q_off + (p.pack_nq > 0 ? r % p.pack_nq : r);
+    }
+    static __device__ __forceinline__ void pos_range(const Params &p, int a, int b, int &lo, int &hi) {
+        b = max(a, b);
+        if (p.pack_nq > 0 && (b - a + 1 >= p.pack_nq || a / p.pack_nq != b / p.pack_nq)) {
+            lo = p.q_off;
+            hi = p.q_off + p.pack_nq - 1;
+        } else {
+            lo = pos_of(p, a);
+            hi = pos_of(p, b);
+        }
+    }
 
     // Issue the direct loads of tile t (keys t*BN ..) into ring stage dst.
     static __device__ __forceinline__ void load_tile(const Ctx &x, int t, char *kdst, char *vdst) {
@@ -99,7 +121,7 @@ struct Kernel {
             const int row = slot / CHUNKS_PER_ROW;
             const int chp = slot % CHUNKS_PER_ROW;
             const int ch = chp ^ swz<D>(row);
-            const int64_t grow = min(j0 + row, x.N - 1);
+            const int64_t grow = min(j0 + row, x.Nk - 1);
             const int64_t off = grow * D + ch * 8;
             const int lds_off = x.kgroup * TILEB + (i * NWQ + x.wave_q) * 1024;
             lds_dma16(x.kp + off, __builtin_amdgcn_readfirstlane(lds_addr(kdst + lds_off)));
@@ -158,9 +180,9 @@ struct Kernel {
     static __device__ __forceinline__ void compute_tile(const Ctx &x, State &st, int t, const char *kl,
                                                         const char *vl) {
         const int j0 = t * BN;
-        const int N = x.N;
-        bool edge = (j0 + BN > N);
-        if constexpr (MASK != MASK_NONE) edge = edge || (j0 + BN - 1 > x.qw0);
+        const int Nk = x.Nk;
+        bool edge = (j0 + BN > Nk);
+        if constexpr (MASK != MASK_NONE) edge = edge || (j0 + BN - 1 > x.pw0);
         if constexpr (MASK == MASK_WINDOW) edge = edge || (j0 < x.w_last - x.window + 1);
 
         // ---- S^T = K . Q^T; K fragments are read two d-steps ahead
@@ -197,8 +219,8 @@ struct Kernel {
         u32x4 ph[QB][KS], pl[QB][KS];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int qi = x.qw0 + qb * 32 + x.l32;
-            int hi = N - 1 - (j0 + 8 * x.g);
+            const int qi = x.lpos[qb];
+            int hi = Nk - 1 - (j0 + 8 * x.g);
             int lo = -(1 << 30);
             if constexpr (MASK != MASK_NONE) hi = min(hi, qi - (j0 + 8 * x.g));
             if constexpr (MASK == MASK_WINDOW) lo = qi - x.window + 1 - (j0 + 8 * x.g);
@@ -223,9 +245,9 @@ struct Kernel {
         if (i + NSTAGE - 1 < my_count) load_tile(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
         if (i < my_count) {
             const int t = my_begin + i;
-            bool any = x.qw0 < x.N;
+            bool any = x.qw0 < x.Nq;
             if constexpr (MASK != MASK_NONE) any = any && (t * BN <= x.w_last);
-            if constexpr (MASK == MASK_WINDOW) any = any && (t * BN + BN - 1 >= x.qw0 - x.window + 1);
+            if constexpr (MASK == MASK_WINDOW) any = any && (t * BN + BN - 1 >= x.pw0 - x.window + 1);
             if (any)
                 compute_tile<EXACT>(x, st, t, x.kst[S] + x.kgroup * TILEB, x.vst[S] + x.kgroup * TILEB);
         }
@@ -252,7 +274,8 @@ struct Kernel {
         x.kgroup = wave / NWQ;
         x.g = x.lane >> 5;
         x.l32 = x.lane & 31;
-        x.N = p.N;
+        x.Nq = p.N;
+        x.Nk = p.Nk;
         x.window = p.window;
         x.c = p.c;
         for (int s = 0; s < NSTAGE; ++s) {
@@ -260,24 +283,30 @@ struct Kernel {
             x.vst[s] = vst[s];
         }
         const int N = p.N;
+        const int Nk = p.Nk;
 
-        // ---- which (batch*head, query tile) this workgroup owns; for masked
-        // runs the heaviest query tiles (most visible keys) are dispatched first.
+        // ---- which (batch*head, key split, query tile) this workgroup owns;
+        // for masked runs the heaviest query tiles (most visible keys) are
+        // dispatched first.
         const int bid = blockIdx.x;
         const int bh = bh_of(bid % p.n_bh, p.n_bh, p.group, p.xcd_kv);
-        const int rank = bid / p.n_bh;
+        const int rest = bid / p.n_bh;
+        const int split = rest % p.n_splits;
+        const int rank = rest / p.n_splits;
         const int qt = (MASK == MASK_NONE) ? rank : masked_qtile(rank, p.n_qtiles, p.zigzag);
         const int b = bh / p.Hq;
         const int h = bh - b * p.Hq;
         const int hkv = p.Hq / p.group;
         const int64_t kvhead = (int64_t)b * hkv + h / p.group;
         const uint16_t *qp = p.q + (int64_t)bh * N * D;
-        x.kp = p.k + kvhead * N * D;
-        x.vp = p.v + kvhead * N * D;
+        x.kp = p.k + kvhead * Nk * D;
+        x.vp = p.v + kvhead * Nk * D;
 
         const int q_tile0 = qt * BM;
         x.qw0 = q_tile0 + x.wave_q * QB * 32;
-        x.w_last = min(x.qw0 + QB * 32, N) - 1;
+        pos_range(p, x.qw0, min(x.qw0 + QB * 32, N) - 1, x.pw0, x.w_last);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) x.lpos[qb] = pos_of(p, x.qw0 + qb * 32 + x.l32);
 
         State st;
         // ---- Q fragments (MFMA B operand): lane holds row qw0 + 32*qb + l32,
@@ -302,20 +331,24 @@ struct Kernel {
                 for (int r = 0; r < 16; ++r) st.oacc[qb][cb][r] = 0.0f;
         }
 
-        // ---- key tiles seen by the workgroup, split between the key groups
-        const int q_last = min(q_tile0 + BM, N) - 1;
-        int kv_lo = 0, kv_hi = N - 1;
-        if constexpr (MASK != MASK_NONE) kv_hi = q_last;
-        if constexpr (MASK == MASK_WINDOW) kv_lo = max(0, q_tile0 - p.window + 1);
-        const int t_begin = kv_lo / BN;
-        const int n_tiles = kv_hi / BN + 1 - t_begin;
+        // ---- key tiles seen by the workgroup (within its key split), divided
+        // between the key groups
+        int p_first, p_last;
+        pos_range(p, q_tile0, min(q_tile0 + BM, N) - 1, p_first, p_last);
+        int kv_lo = 0, kv_hi = Nk - 1;
+        if constexpr (MASK != MASK_NONE) kv_hi = min(kv_hi, p_last);
+        if constexpr (MASK == MASK_WINDOW) kv_lo = max(0, p_first - p.window + 1);
+        const int s_first = p.split_t0 + split * p.split_tiles;
+        const int t_begin = max(kv_lo / BN, s_first);
+        const int t_last = min(kv_hi / BN, s_first + p.split_tiles - 1);
+        const int n_tiles = max(0, t_last + 1 - t_begin);
         const int half = (n_tiles + KSPLIT - 1) / KSPLIT;
         const int my_begin = t_begin + x.kgroup * half;
         const int my_count = max(0, min(half, n_tiles - x.kgroup * half));
 
         // ---- two-term P for query tiles whose first row sees few keys
-        int min_vis = N;
-        if constexpr (MASK != MASK_NONE) min_vis = min(N, q_tile0 + 1);
+        int min_vis = Nk;
+        if constexpr (MASK != MASK_NONE) min_vis = min(Nk, p_first + 1);
         if constexpr (MASK == MASK_WINDOW) min_vis = min(min_vis, p.window);
         const bool exact = min_vis < p.exact_below;
 
@@ -376,6 +409,37 @@ struct Kernel {
                         st.oacc[qb][cb][r] = st.oacc[qb][cb][r] * a0 + src[(base * 16 + r) * 64 + x.lane] * a1;
                 }
             }
+        }
+
+        // ---- epilogue of one key split: O / l in fp32 and m + log2 l go to
+        // the workspace for the merge kernel (a row that saw no key of this
+        // split gives O = 0 and -inf)
+        if (p.n_splits > 1) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float lt = sum_halves(st.lsum[qb]);
+                const int qi = x.qw0 + qb * 32 + x.l32;
+                if (qi < N) {
+                    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+                    const int64_t prow = ((int64_t)split * p.n_bh + bh) * N + qi;
+                    float *orow = p.ws_o + prow * D;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                        for (int j4 = 0; j4 < 4; ++j4) {
+                            const int ch = cb * 32 + 8 * j4 + 4 * x.g;
+                            float4 w;
+                            w.x = st.oacc[qb][cb][4 * j4 + 0] * inv;
+                            w.y = st.oacc[qb][cb][4 * j4 + 1] * inv;
+                            w.z = st.oacc[qb][cb][4 * j4 + 2] * inv;
+                            w.w = st.oacc[qb][cb][4 * j4 + 3] * inv;
+                            *(float4 *)(orow + ch) = w;
+                        }
+                    if (x.g == 0)
+                        p.ws_ml[prow] = lt > 0.0f ? st.mrun[qb] + __builtin_amdgcn_logf(lt) : -__builtin_inff();
+                }
+            }
+            return;
         }
 
         // ---- epilogue: O = acc / l, rounded once; LSE = ln 2 * (m + log2 l)

@@ -74,7 +74,8 @@ typedef enum {
     ATTN_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     ATTN_ERR_ALIAS = 6,       /* o or lse overlaps q, k, v or each other */
     ATTN_ERR_LAUNCH = 7,      /* the kernel launch itself failed */
-    ATTN_ERR_DEVICE = 8       /* no usable gfx950 device is current */
+    ATTN_ERR_DEVICE = 8,      /* no usable gfx950 device is current */
+    ATTN_ERR_WORKSPACE = 9    /* split-KV workspace smaller than attn_fwd_splitkv_workspace_size */
 } attn_status_t;
 
 /*
@@ -118,7 +119,8 @@ int attn_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int 
  * desc[0..5] = {32-row query blocks per wave, waves per workgroup, keys per
  * K/V tile, query rows per workgroup, key groups per workgroup, depth of the
  * LDS tile ring}.  attn_fwd_config_desc returns ATTN_ERR_ARG for a bad id, a
- * bad d or a NULL desc.
+ * bad d or a NULL desc, and ATTN_ERR_UNSUPPORTED for a configuration not built
+ * for that d (the ping-pong ids 4 and 5 exist for d = 64 only).
  */
 int attn_fwd_num_configs(void);
 int attn_fwd_config_desc(int id, int64_t d, int64_t *desc);
@@ -134,13 +136,107 @@ int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
  * attn_fwd with an explicit tile configuration (config_id in
  * [0, attn_fwd_num_configs()), or -1 for the automatic choice that attn_fwd
  * makes).  Same semantics, layout, ownership and errors as attn_fwd, plus
- * ATTN_ERR_ARG for a bad config_id.  Every configuration computes the same
+ * ATTN_ERR_ARG for a bad config_id and ATTN_ERR_UNSUPPORTED for one not built
+ * for this d (attn_fwd_config_desc says which).  Every configuration computes the same
  * function; they differ only in speed.
  */
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                 int causal, int64_t window, float scale, int dtype, int config_id,
                 void *stream);
+
+/*
+ * ---- Split-KV forward ("FlashDecoding") ----------------------------------
+ *
+ * The same operation for Nq query rows against Nk keys, with the key range cut
+ * into chunks that separate workgroups process in parallel, as in
+ * "Optimizaciones de Atencion", section "FlashDecoding": (1) the keys are
+ * divided into P chunks of about Nk / P tokens (here whole K/V tiles), (2) each
+ * chunk yields, per query row, its local row max m_p, local sum l_p and the
+ * partial output normalised within the chunk, and (3) a second kernel merges
+ * them: global max m = max_p m_p, each partial output weighted by
+ * exp(m_p - m) * l_p, divided by the sum of those weights; the row's
+ * log-sum-exp is m + ln of that sum.  The result is the exact attention of
+ * attn_fwd (it differs only in rounding).  It fills the GPU when B * Hq * Nq
+ * is small: decoding (Nq = 1 or a few new tokens against a long cached
+ * sequence) and short prefill grids.
+ *
+ * Visibility with Nq != Nk: the queries are the last Nq positions of the
+ * sequence (bottom-right alignment; the pages do not fix this): query row i
+ * sits at position p = Nk - Nq + i, and key j is visible iff
+ *   causal == 0 : always (window must then be 0);
+ *   causal != 0 : j <= p, and when window > 0 also p - j < window.
+ * causal != 0 requires Nq <= Nk (else the first rows would see no key).  With
+ * Nq == Nk this is exactly attn_fwd.
+ *
+ * Layout: q, o (B, Hq, Nq, d); k, v (B, Hkv, Nk, d); lse (B, Hq, Nq) float32,
+ * may be NULL; all row-major, contiguous, device memory, 16-bit `dtype`.
+ *
+ * Workspace: the library allocates nothing.  When the call uses more than one
+ * chunk it needs a caller-owned device buffer `workspace` of at least
+ * attn_fwd_splitkv_workspace_size(...) bytes, 16-byte aligned, disjoint from
+ * every input and output, alive until the stream passes the call; it holds
+ * the fp32 partial outputs (chunks x B*Hq*Nq x d) and partial log-sum-exps
+ * (chunks x B*Hq*Nq).  Nothing in it needs clearing before the call, and its
+ * contents afterwards are unspecified.  Calls that share a workspace must be
+ * ordered on one stream.  With one chunk the workspace is not touched and may
+ * be NULL.
+ *
+ * num_splits: the number of chunks wanted, 1 .. 1024, or 0 for the automatic
+ * choice (enough workgroups to fill the GPU, at least four K/V tiles per
+ * chunk).  The count used is ceil(key tiles / tiles per chunk) with tiles per
+ * chunk = ceil(key tiles / num_splits), so it never exceeds num_splits nor the
+ * number of key tiles.
+ *
+ * Errors (checked on the host before anything is enqueued; on error nothing
+ * is launched and o, lse and the workspace are untouched): those of attn_fwd
+ * with N read as Nq, plus ATTN_ERR_SHAPE for Nk < 0, Nk == 0 < Nq or causal
+ * with Nq > Nk; ATTN_ERR_ARG for num_splits outside [0, 1024] or a bad
+ * config_id; ATTN_ERR_UNSUPPORTED for a configuration of a kernel kind other
+ * than the lockstep one (ids 4, 5, 6); ATTN_ERR_NULL for a NULL workspace
+ * when more than one chunk is used; ATTN_ERR_WORKSPACE when workspace_bytes
+ * is too small; ATTN_ERR_ALIGN for a misaligned workspace; ATTN_ERR_ALIAS when
+ * it overlaps an input or output.  Enqueues two kernels (attention, then the
+ * merge) on `stream`, or one when a single chunk is used.
+ */
+int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                     int causal, int64_t window, float scale, int dtype, int64_t num_splits,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+
+/* attn_fwd_splitkv with an explicit tile configuration (-1 = automatic:
+ * configuration 8, one-wave 32-row workgroups, for Nq <= 32, else the choice
+ * attn_fwd makes). */
+int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                        int causal, int64_t window, float scale, int dtype, int64_t num_splits,
+                        int config_id, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace a split-KV call with these arguments needs (0 when it
+ * uses one chunk), or minus the status code when the sizes are invalid.  Pure
+ * host computation. */
+int64_t attn_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                        int64_t d, int causal, int64_t window, int dtype,
+                                        int64_t num_splits, int config_id);
+
+/* The host-side checks of attn_fwd_splitkv_ex alone (no HIP call, no memory
+ * behind the pointers touched). */
+int attn_fwd_splitkv_validate(const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                              int64_t Nk, int64_t d, int causal, int64_t window, float scale, int dtype,
+                              int64_t num_splits, int config_id, const void *workspace,
+                              int64_t workspace_bytes);
+
+/* What a split-KV call would launch: writes 9 integers to plan (may be NULL)
+ * -- query rows per workgroup, keys per K/V tile, waves per workgroup,
+ * workgroups of the attention kernel, chunks used, K/V tiles per chunk,
+ * configuration id, workspace bytes, and 1 when the G query heads of each K/V
+ * head are stacked into one tile (G > 1 and Nq <= 16: each K/V tile is then
+ * read once for all G heads), else 0 -- and returns the status of the size
+ * checks. */
+int attn_fwd_splitkv_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                          int causal, int64_t window, int dtype, int64_t num_splits, int config_id,
+                          int64_t *plan);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,37 @@ def run_gpu(q, k, v, *, causal, window=0, scale=None, config_id=-1, poison=True)
     return o.cpu(), lse.cpu()
 
 
+def run_gpu_splitkv(q, k, v, *, causal, window=0, scale=None, num_splits=0, config_id=-1, poison=True,
+                    workspace=None):
+    """Host tensors q (B,Hq,Nq,d), k/v (B,Hkv,Nk,d) in, (o, lse) host tensors
+    out, via attn_fwd_splitkv_ex.  The workspace is allocated here (filled
+    with NaN bit patterns when poison is set) unless one is passed."""
+    import flashattention_forward_05_amd as fa
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    dtype = DT_CODE["f16" if q.dtype == torch.float16 else "bf16"]
+    need = fa.attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits,
+                                              config_id)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        if poison:
+            workspace.fill_(0xFF)
+    if poison:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    fa.attn_fwd_splitkv_ex(qd, kd, vd, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                           num_splits, config_id, workspace, workspace.numel(),
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
 def oracle_full(q, k, v, *, causal, window=0, scale=None):
     d = q.shape[-1]
     if scale is None:

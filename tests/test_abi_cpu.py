@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         assert fa.attn_status_str(code) and fa.attn_status_str(code) != "unknown status"
     assert fa.attn_status_str(99) == "unknown status"
 
@@ -85,6 +85,14 @@ def test_plan_reports_tiles():
     assert fa.attn_fwd_plan(1, 32, 1, 32768, 128, 1, 4096, 1)["mask_mode"] == 2
     for d in (64, 128):
         for cid in range(fa.attn_fwd_num_configs()):
+            if d == 128 and cid in (4, 5):      # ping-pong is built for d = 64 only
+                with pytest.raises(fa.AttnError) as e:
+                    fa.attn_fwd_config_desc(cid, d)
+                assert e.value.status == 3
+                with pytest.raises(fa.AttnError) as e:
+                    fa.attn_fwd_plan_ex(2, 4, 4, 1000, d, 1, 0, 0, cid)
+                assert e.value.status == 3
+                continue
             desc = fa.attn_fwd_config_desc(cid, d)
             assert desc["block_m"] * desc["key_groups"] == 32 * desc["query_blocks_per_wave"] * desc["waves"]
             pe = fa.attn_fwd_plan_ex(2, 4, 4, 1000, d, 1, 0, 0, cid)
@@ -121,3 +129,76 @@ def test_auto_config_choice():
     assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 2      # GQA prefill
     assert auto(1, 32, 1, 32768, 128, 1, 4096, 1) == 2  # MQA with window
     assert auto(1, 2, 2, 512, 128, 1, 0, 1) == 1        # small d=128 grid
+
+
+# ---- split-KV entry points (host checks, plan, workspace size)
+G = 1 << 30          # room for every buffer of the split-KV shapes below
+KV = dict(q=G, k=2 * G, v=3 * G, o=4 * G, lse=5 * G, B=2, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128,
+          causal=1, window=0, scale=0.125, dtype=1, num_splits=0, config_id=-1, workspace=6 * G,
+          workspace_bytes=1 << 20)
+
+
+def validate_kv(**over):
+    a = dict(KV, **over)
+    return fa.attn_fwd_splitkv_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                        a["Nq"], a["Nk"], a["d"], a["causal"], a["window"], a["scale"],
+                                        a["dtype"], a["num_splits"], a["config_id"], a["workspace"],
+                                        a["workspace_bytes"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, 0),
+    ({"lse": None}, 0),
+    ({"Nq": 0, "q": None, "k": None, "v": None, "o": None, "workspace": None}, 0),
+    ({"num_splits": 1, "workspace": None, "workspace_bytes": 0}, 0),      # one chunk: no workspace
+    ({"Nq": 4096, "num_splits": 1, "workspace": None}, 0),
+    ({"causal": 0, "Nq": 5000}, 0),                                     # non-causal may have Nq > Nk
+    ({"q": None}, 1), ({"workspace": None}, 1),
+    ({"Nk": 0}, 2), ({"Nk": -1}, 2), ({"Nq": 4097}, 2), ({"Nk": (1 << 24) + 1}, 2), ({"Hq": 3}, 2),
+    ({"d": 96}, 3), ({"config_id": 4}, 3), ({"config_id": 6}, 3), ({"window": 8, "causal": 0}, 3),
+    ({"num_splits": -1}, 4), ({"num_splits": 1025}, 4), ({"config_id": 9}, 4), ({"scale": float("nan")}, 4),
+    ({"workspace": 6 * G + 8}, 5), ({"q": G + 2}, 5),
+    ({"o": 2 * G}, 6), ({"workspace": 3 * G}, 6), ({"workspace": 5 * G}, 6), ({"workspace": 4 * G - 64}, 6),
+    ({"workspace_bytes": 64}, 9),
+])
+def test_splitkv_validate_codes(over, code):
+    assert validate_kv(**over) == code
+
+
+def test_splitkv_plan_and_workspace():
+    # decoding: the 4 query heads of each K/V head stacked into one 32-row
+    # workgroup per chunk, automatic chunk count
+    p = fa.attn_fwd_splitkv_plan(4, 32, 8, 1, 8192, 128, 1, 0, 1)
+    assert p["config_id"] == 8 and p["block_m"] == 32 and p["waves"] == 1 and p["stacked"] == 1
+    key_tiles = 8192 // p["block_n"]
+    assert p["n_splits"] > 1 and p["split_tiles"] >= 4
+    assert p["n_splits"] == -(-key_tiles // p["split_tiles"])
+    assert p["grid"] == 4 * 8 * p["n_splits"]
+    # stacking needs G > 1 and at most 16 query rows; then G * Nq rows per K/V head
+    m = fa.attn_fwd_splitkv_plan(1, 32, 1, 3, 4096, 128, 1, 0, 1, 2)
+    assert m["stacked"] == 1 and m["grid"] == -(-96 // m["block_m"]) * m["n_splits"]
+    assert fa.attn_fwd_splitkv_plan(1, 8, 2, 17, 4096, 64, 1, 0, 0, 2)["stacked"] == 0
+    assert fa.attn_fwd_splitkv_plan(1, 8, 8, 1, 4096, 64, 1, 0, 0, 2)["stacked"] == 0
+    assert p["workspace_bytes"] == p["n_splits"] * 4 * 32 * 1 * (128 + 1) * 4
+    assert fa.attn_fwd_splitkv_workspace_size(4, 32, 8, 1, 8192, 128, 1, 0, 1) == p["workspace_bytes"]
+    # explicit chunk counts: ceil(tiles / ceil(tiles / P)) chunks, never more than the tiles
+    for want in (1, 2, 3, 7, 64, 1000):
+        q = fa.attn_fwd_splitkv_plan(1, 1, 1, 1, 1000, 64, 1, 0, 0, want)
+        tiles = -(-1000 // q["block_n"])
+        per = -(-tiles // min(want, tiles))
+        assert q["split_tiles"] == per and q["n_splits"] == -(-tiles // per)
+        assert q["workspace_bytes"] == (0 if q["n_splits"] == 1 else q["n_splits"] * (64 + 1) * 4)
+    # a window: chunks cover only the 4096 keys the query sees
+    wnd = fa.attn_fwd_splitkv_plan(1, 32, 1, 1, 32768, 128, 1, 4096, 1)
+    vis_tiles = 4096 // wnd["block_n"]
+    assert wnd["n_splits"] == -(-vis_tiles // wnd["split_tiles"]) and wnd["n_splits"] > 1
+    # square prefill shapes take the plain forward's tile choice and, on grids
+    # of 64 workgroups or more, one chunk
+    assert fa.attn_fwd_splitkv_plan(2, 4, 4, 1024, 1024, 64, 1, 0, 0)["n_splits"] == 1
+    assert fa.attn_fwd_splitkv_plan(2, 4, 4, 1024, 1024, 64, 1, 0, 0)["config_id"] == 7
+    with pytest.raises(fa.AttnError) as e:                       # the C call returns -status
+        fa.attn_fwd_splitkv_workspace_size(1, 3, 2, 1, 10, 64, 1, 0, 0)
+    assert e.value.status == 2
+    assert fa.load_library().attn_fwd_splitkv_workspace_size(1, 3, 2, 1, 10, 64, 1, 0, 0, 0, -1) == -2
+    with pytest.raises(fa.AttnError):
+        fa.attn_fwd_splitkv_plan(1, 1, 1, 8, 4, 64, 1, 0, 0)    # causal with Nq > Nk

@@ -99,6 +99,11 @@ def test_ragged_all_configs(fa, case):
     q, k, v = inputs(B, Hq, Hkv, N, d, dt, seed=N)
     ro, rl = oracle_full(q, k, v, causal=causal, window=window)
     for cfg in range(fa.attn_fwd_num_configs()):
+        if d == 128 and cfg in (4, 5):          # ping-pong is built for d = 64 only
+            with pytest.raises(fa.AttnError) as e:
+                run_gpu(q, k, v, causal=causal, window=window, config_id=cfg)
+            assert e.value.status == 3
+            continue
         o, lse = run_gpu(q, k, v, causal=causal, window=window, config_id=cfg)
         check(f"cfg{cfg}", o, lse, ro, rl, dt)
 
