@@ -197,9 +197,10 @@ def summarize_counters(dirs: dict) -> dict:
 
 
 def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, label):
-    """HBM bytes per launch of the attention kernel from FETCH_SIZE/WRITE_SIZE
-    (KiB per dispatch), each scaled by what the same counter reads for a plain
-    copy of copy_mib MiB."""
+    """HBM bytes per call of the attention library from FETCH_SIZE/WRITE_SIZE
+    (KiB per dispatch, summed over the kernels of one call), each scaled by
+    what the same counter reads for a plain copy of copy_mib MiB.  The counter
+    runs must profile a workload with a single variant."""
     f = summarize_counters({"f": fetch_dir})
     w = summarize_counters({"w": write_dir})
     cf = summarize_counters({"cf": copy_fetch_dir})
@@ -209,8 +210,10 @@ def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mi
     cw_kib = max(v for (k, c), v in cw.items() if c == "WRITE_SIZE" and "copy" in k.lower())
     fscale = known / (cf_kib * 1024)
     wscale = known / (cw_kib * 1024)
-    kf = [v for (k, c), v in f.items() if c == "FETCH_SIZE" and "attn_fwd" in k][0]
-    kw = [v for (k, c), v in w.items() if c == "WRITE_SIZE" and "attn_fwd" in k][0]
+    # one call may launch two kernels (split-KV: attention, then the merge):
+    # the per-dispatch means of every attention-library kernel are summed
+    kf = sum(v for (k, c), v in f.items() if c == "FETCH_SIZE" and "attn_fwd" in k)
+    kw = sum(v for (k, c), v in w.items() if c == "WRITE_SIZE" and "attn_fwd" in k)
     return {"label": label, "fetch_kib_raw": kf, "write_kib_raw": kw, "fetch_scale": fscale,
             "write_scale": wscale, "hbm_read_bytes": kf * 1024 * fscale,
             "hbm_write_bytes": kw * 1024 * wscale,
