@@ -106,6 +106,40 @@ def make_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "f16",
     return q.to(tdt).contiguous(), k.to(tdt).contiguous(), v.to(tdt).contiguous()
 
 
+def make_paged_cache(k: torch.Tensor, v: torch.Tensor, page_size: int, seq_lens, seed: int = 0,
+                     spare_pages: int = 3):
+    """Scatter contiguous host K/V (B, Hkv, Nmax, d) into page pools
+    (num_pages, Hkv, page_size, d) through a seeded random page table, the
+    layout of the paged forward: request b's keys 0 .. seq_lens[b]-1 fill
+    ceil(seq_lens[b] / page_size) pages taken from a random permutation of
+    the pool.  Slots past a request's length and spare pages hold NaN, so any
+    read of them would show in the output; table entries past a request's
+    pages are -1.  Returns (k_pool, v_pool, block_table int32 (B, max_pages),
+    seq_lens int32 (B,))."""
+    B, Hkv, nmax, d = k.shape
+    lens = [int(x) for x in seq_lens]
+    assert len(lens) == B and all(0 <= n <= nmax for n in lens)
+    per = [-(-n // page_size) for n in lens]
+    max_pages = max(1, -(-nmax // page_size))
+    total = sum(per) + spare_pages
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    perm = torch.randperm(total, generator=g).tolist()
+    k_pool = torch.full((total, Hkv, page_size, d), float("nan"), dtype=k.dtype)
+    v_pool = torch.full((total, Hkv, page_size, d), float("nan"), dtype=v.dtype)
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    n = 0
+    for b in range(B):
+        for pg in range(per[b]):
+            page = perm[n]
+            n += 1
+            table[b, pg] = page
+            lo, hi = pg * page_size, min((pg + 1) * page_size, lens[b])
+            k_pool[page, :, :hi - lo] = k[b, :, lo:hi]
+            v_pool[page, :, :hi - lo] = v[b, :, lo:hi]
+    return k_pool.contiguous(), v_pool.contiguous(), table, torch.tensor(lens, dtype=torch.int32)
+
+
 def make_workload(w: Workload, seed: int = 0):
     return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed, w.amplitude,
                     nk=None if w.nk == w.N else w.nk)

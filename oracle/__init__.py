@@ -60,6 +60,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_oracle_rows_qk.restype = ctypes.c_int
     lib.attn_oracle_rows_qk.argtypes = [vp, vp, vp, vp, i64, dp, dp, i64, i64, i64, i64, i64, i64,
                                         ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_fwd_paged.restype = ctypes.c_int
+    lib.attn_oracle_fwd_paged.argtypes = [vp, vp, vp, vp, vp, dp, dp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                          ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
     lib.attn_oracle_decode.restype = ctypes.c_double
     lib.attn_oracle_decode.argtypes = [ctypes.c_uint16, ctypes.c_int]
     lib.attn_oracle_max_threads.restype = ctypes.c_int
@@ -133,6 +136,31 @@ def oracle_rows(q, k, v, row_ids, *, scale: float, causal: bool = False, window:
                                  int(bool(causal)), int(window), float(scale), DTYPES[dtype])
     if rc != 0:
         raise RuntimeError(f"attn_oracle_rows failed with code {rc}")
+    return o, lse
+
+
+def oracle_paged(q, k_pool, v_pool, block_table, seq_lens, *, scale: float, causal: bool = False,
+                 window: int = 0, dtype: str = "f16", lib: ctypes.CDLL | None = None):
+    """Paged K/V forward in fp64.  q (B,Hq,Nq,d); pools (num_pages,Hkv,page_size,d)
+    as uint16 bit patterns ("f16"/"bf16") or float64 ("f64"); block_table
+    (B,max_pages) and seq_lens (B,) int32.  Returns (o (B,Hq,Nq,d), lse
+    (B,Hq,Nq)) as float64."""
+    lib = lib or load_library()
+    q, k_pool, v_pool = (_as_input(x, dtype) for x in (q, k_pool, v_pool))
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_pool.shape
+    if v_pool.shape != k_pool.shape or dk != d or bt.ndim != 2 or bt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("paged oracle: inconsistent shapes")
+    o = np.zeros((B, Hq, Nq, d), np.float64)
+    lse = np.zeros((B, Hq, Nq), np.float64)
+    rc = lib.attn_oracle_fwd_paged(q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data, bt.ctypes.data,
+                                   sl.ctypes.data, o.ctypes.data, lse.ctypes.data, B, Hq, Hkv, Nq, d, page_size,
+                                   num_pages, bt.shape[1], int(bool(causal)), int(window), float(scale),
+                                   DTYPES[dtype])
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_fwd_paged failed with code {rc}")
     return o, lse
 
 

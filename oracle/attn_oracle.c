@@ -39,6 +39,14 @@
  *  - A row with no visible key (unreachable through the library's argument
  *    rules) yields o = 0 and lse = -inf, the limit of the all-masked-row guard
  *    in "Lab 02", "Errores tipicos".
+ *  - Paged K/V ("00 - Por que la atencion domina la inferencia", section
+ *    "PagedAttention es un problema distinto": the cache lives in fixed-size
+ *    blocks with a table of blocks per request, and the kernel follows the
+ *    table).  Reading taken for the layout: pools (num_pages, Hkv, page_size,
+ *    d); key j of request b is slot j % page_size of page
+ *    block_table[b][j / page_size]; request b has seq_lens[b] keys.  The
+ *    oracle walks the table to gather each request's keys in order and then
+ *    applies the definition above.
  *  - Fewer queries than keys (Nq < Nk, the decoding case of "Optimizaciones de
  *    Atencion", section "FlashDecoding": a few new query tokens against a
  *    cached sequence): the pages do not say how the causal mask aligns.
@@ -281,4 +289,71 @@ int attn_oracle_rows(const void *q, const void *k, const void *v,
 {
     return attn_oracle_rows_qk(q, k, v, row_ids, nrows, o, lse, B, Hq, Hkv, N, N, d,
                                causal, window, scale, dtype);
+}
+
+/*
+ * Paged K/V forward.  q, o: (B, Hq, Nq, d); k_pool, v_pool: (num_pages, Hkv,
+ * page_size, d); block_table: (B, max_pages) int32; seq_lens: (B,) int32;
+ * lse: (B, Hq, Nq).  For each request b the keys 0 .. seq_lens[b]-1 are
+ * gathered by walking its page table (key j: page block_table[b][j /
+ * page_size], slot j % page_size) into contiguous (1, Hkv, seq_lens[b], d)
+ * arrays, and the Nq-against-Nk forward above runs on them.  Returns 0, -1 on
+ * bad arguments or a table entry outside [0, num_pages), -2 when memory cannot
+ * be allocated.
+ */
+int attn_oracle_fwd_paged(const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *block_table, const int32_t *seq_lens,
+                          double *o, double *lse,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t d,
+                          int64_t page_size, int64_t num_pages, int64_t max_pages,
+                          int causal, int64_t window, float scale, int dtype)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || d < 1 || Hq % Hkv != 0 || page_size < 1 ||
+        num_pages < 1 || max_pages < 1 || window < 0 || dtype < ORACLE_F16 || dtype > ORACLE_F64)
+        return -1;
+    size_t esize = dtype == ORACLE_F64 ? sizeof(double) : sizeof(uint16_t);
+    for (int64_t b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > max_pages * page_size)
+            return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t nk = seq_lens[b];
+        size_t rows = (size_t)(Hkv * (nk > 0 ? nk : 1));
+        char *kg = (char *)malloc(rows * (size_t)d * esize);
+        char *vg = (char *)malloc(rows * (size_t)d * esize);
+        if (!kg || !vg) {
+            free(kg);
+            free(vg);
+            return -2;
+        }
+        int bad = 0;
+        for (int64_t hk = 0; hk < Hkv && !bad; ++hk)
+            for (int64_t j = 0; j < nk; ++j) {
+                int64_t page = block_table[b * max_pages + j / page_size];
+                if (page < 0 || page >= num_pages) {
+                    bad = 1;
+                    break;
+                }
+                int64_t src = ((page * Hkv + hk) * page_size + j % page_size) * d;
+                int64_t dst = (hk * nk + j) * d;
+                memcpy(kg + (size_t)dst * esize, (const char *)k_pool + (size_t)src * esize, (size_t)d * esize);
+                memcpy(vg + (size_t)dst * esize, (const char *)v_pool + (size_t)src * esize, (size_t)d * esize);
+            }
+        const char *qb = (const char *)q + (size_t)(b * Hq * Nq * d) * esize;
+        int rc = bad ? -1 : 0;
+        if (!bad && nk > 0) {
+            rc = attn_oracle_fwd_qk(qb, kg, vg, o + b * Hq * Nq * d, lse + b * Hq * Nq,
+                                    1, Hq, Hkv, Nq, nk, d, causal, window, scale, dtype);
+        } else if (!bad) {
+            for (int64_t r = 0; r < Hq * Nq; ++r) {
+                for (int64_t c = 0; c < d; ++c)
+                    o[(b * Hq * Nq + r) * d + c] = 0.0;
+                lse[b * Hq * Nq + r] = -INFINITY;
+            }
+        }
+        free(kg);
+        free(vg);
+        if (rc != 0)
+            return rc;
+    }
+    return 0;
 }

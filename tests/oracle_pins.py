@@ -422,6 +422,72 @@ def pin_split_kv_merge(lib):
                 close(lse[0, 0], sl, 1e-13, f"oracle vs split lse P={n_splits}")
 
 
+def pin_paged_matches_contiguous(lib):
+    """Walking a random page table gives exactly the result of the same keys
+    laid out contiguously (ragged lengths per request, every mask, GQA, page
+    sizes below and above the lengths); NaN-filled unused slots are never
+    read."""
+    from attn_inputs import make_paged_cache
+    for (B, Hq, Hkv, Nq, lens, d, ps, dtype, seed) in [(3, 4, 2, 1, (37, 5, 64), 8, 16, "f16", 61),
+                                                       (2, 2, 1, 3, (40, 17), 4, 8, "bf16", 62),
+                                                       (1, 3, 3, 2, (9,), 8, 64, "f16", 63)]:
+        nmax = max(lens)
+        q, k, v = make_qkv(B, Hq, Hkv, Nq, d, dtype, seed=seed, nk=nmax)
+        kp, vp, bt, sl = make_paged_cache(k, v, ps, lens, seed=seed)
+        qb = to_bits(q)
+        for causal, window in MASKS:
+            o, lse = oracle.oracle_paged(qb, to_bits(kp), to_bits(vp), bt.numpy(), sl.numpy(), scale=0.3,
+                                         causal=causal, window=window, dtype=dtype, lib=lib)
+            assert np.isfinite(o).all()
+            for b in range(B):
+                kb = np.ascontiguousarray(to_bits(k)[b:b + 1, :, :lens[b]])
+                vb = np.ascontiguousarray(to_bits(v)[b:b + 1, :, :lens[b]])
+                ob, lb = run(lib, np.ascontiguousarray(qb[b:b + 1]), kb, vb, 0.3, causal, window, dtype)
+                close(o[b:b + 1], ob, 0.0, f"paged o b={b} causal={causal} W={window}")
+                close(lse[b:b + 1], lb, 0.0, f"paged lse b={b} causal={causal} W={window}")
+
+
+def pin_paged_gather_order(lib):
+    """Closed form that fixes the page walk: with K = 0 every visible key has
+    the same weight, and V rows that encode (request, K/V head, key index)
+    give O = the mean code over the visible keys of that request and head,
+    LSE = ln(count).  A wrong page, slot or head shows up as a wrong mean."""
+    B, Hq, Hkv, Nq, d, ps = 2, 4, 2, 2, 2, 8
+    lens = (29, 11)
+    nmax = max(lens)
+    q = np.random.default_rng(5).standard_normal((B, Hq, Nq, d))
+    k = torch.zeros((B, Hkv, nmax, d), dtype=torch.float64)
+    v = torch.zeros((B, Hkv, nmax, d), dtype=torch.float64)
+    for b in range(B):
+        for hk in range(Hkv):
+            for j in range(nmax):
+                v[b, hk, j, 0] = 1000.0 * b + 100.0 * hk + j
+                v[b, hk, j, 1] = j * j
+    kp, vp, bt, sl = make_paged_cache_f64(k, v, ps, lens, seed=9)
+    for causal, window in MASKS:
+        o, lse = oracle.oracle_paged(f64(q), f64(kp), f64(vp), bt, sl, scale=0.7, causal=causal, window=window,
+                                     dtype="f64", lib=lib)
+        for b in range(B):
+            for h in range(Hq):
+                hk = h // (Hq // Hkv)
+                for i in range(Nq):
+                    pos = lens[b] - Nq + i
+                    hi = pos if causal else lens[b] - 1
+                    lo = max(0, pos - window + 1) if window > 0 else 0
+                    js = list(range(lo, hi + 1))
+                    want0 = sum(1000.0 * b + 100.0 * hk + j for j in js) / len(js)
+                    want1 = sum(j * j for j in js) / len(js)
+                    close([o[b, h, i, 0], o[b, h, i, 1]], [want0, want1], 1e-9, f"gather b={b} h={h} i={i}")
+                    close([lse[b, h, i]], [math.log(len(js))], 1e-14, "gather lse")
+
+
+def make_paged_cache_f64(k, v, ps, lens, seed):
+    """make_paged_cache on float64 tensors, as numpy arrays."""
+    from attn_inputs import make_paged_cache
+    kp, vp, bt, sl = make_paged_cache(k, v, ps, lens, seed=seed)
+    return kp.numpy(), vp.numpy(), bt.numpy(), sl.numpy()
+
+
 ALL_PINS = [
     pin_decoders,
     pin_tiled_demo,
@@ -441,4 +507,6 @@ ALL_PINS = [
     pin_decode_is_tail_of_square,
     pin_decode_brute_force,
     pin_split_kv_merge,
+    pin_paged_matches_contiguous,
+    pin_paged_gather_order,
 ]

@@ -24,6 +24,12 @@ MUTANTS = {
     "window_condition_off": ("if (window > 0 && pos - window + 1 > 0)", "if (window > 0 && pos - window > 0)"),
     "decode_top_left": ("int64_t pos = Nk - Nq + i;", "int64_t pos = i;"),
     "decode_offset_one_short": ("int64_t pos = Nk - Nq + i;", "int64_t pos = Nk - Nq + i - 1;"),
+    "paged_slot_from_page_index": ("int64_t src = ((page * Hkv + hk) * page_size + j % page_size) * d;",
+                                   "int64_t src = ((page * Hkv + hk) * page_size + j / page_size) * d;"),
+    "paged_head_major_pool": ("int64_t src = ((page * Hkv + hk) * page_size + j % page_size) * d;",
+                              "int64_t src = ((hk * Hkv + page) * page_size + j % page_size) * d;"),
+    "paged_table_by_slot": ("int64_t page = block_table[b * max_pages + j / page_size];",
+                            "int64_t page = block_table[b * max_pages + j % page_size];"),
     "kv_head_stride_uses_nq": ("int64_t kvhead = (b * Hkv + hk) * Nk * d;",
                                "int64_t kvhead = (b * Hkv + hk) * Nq * d;"),
     "gqa_modulo_map": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
@@ -59,6 +65,7 @@ def test_pins_catch_mutant(name, tmp_path):
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(lib)
-        except AssertionError as e:
+        except (AssertionError, RuntimeError, ValueError) as e:
+            # a pin that fails, or an oracle that rejects what it computes
             caught.append(f"{pin.__name__}: {str(e)[:80]}")
     assert caught, f"no pin caught mutant {name}"
