@@ -232,6 +232,9 @@ def main() -> int:
     ap.add_argument("--splitkv", action="store_true",
                     help="run every variant through the split-KV entry point (decoding workloads always are)")
     ap.add_argument("--splits", type=int, default=0, help="key chunks for split-KV calls (0: automatic)")
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                    help="keep the K/V of decoding workloads in pages of this many tokens (random page order) "
+                         "and run the paged entry point")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a summary of a rocprofv3 kernel-trace CSV dir")
@@ -272,7 +275,7 @@ def main() -> int:
     import torch
 
     import flashattention_forward_05_amd as fa
-    from attn_inputs import WORKLOADS, make_workload
+    from attn_inputs import WORKLOADS, make_paged_cache, make_workload
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -295,13 +298,24 @@ def main() -> int:
     # inputs resident in HBM before timing
     runs = []
     for w in wls:
-        q, k, v = (t.to(dev) for t in make_workload(w, seed=0))
+        qh, kh, vh = make_workload(w, seed=0)
+        dt = 0 if w.dtype == "f16" else 1
+        paged = None
+        if args.paged and w.nk != w.N:
+            # every request holds the full cache length; pages in seeded random order
+            kp, vp, bt, sl = make_paged_cache(kh, vh, args.paged, [w.nk] * w.B, seed=0, spare_pages=0)
+            kh, vh = kp, vp
+            paged = dict(bt=bt.to(dev), sl=sl.to(dev), ps=args.paged, num_pages=kp.shape[0], max_pages=bt.shape[1])
+        q, k, v = (t.to(dev) for t in (qh, kh, vh))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-        dt = 0 if w.dtype == "f16" else 1
         split = args.splitkv or w.nk != w.N
         ws = None
-        if split:
+        if paged:
+            plan = fa.attn_fwd_paged_plan(w.B, w.Hq, w.Hkv, w.N, w.d, paged["ps"], paged["num_pages"],
+                                          paged["max_pages"], w.nk, w.causal, w.window, dt, args.splits, args.config)
+            ws = torch.empty(max(16, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
+        elif split:
             plan = fa.attn_fwd_splitkv_plan(w.B, w.Hq, w.Hkv, w.N, w.nk, w.d, w.causal, w.window, dt,
                                             args.splits, args.config)
             ws = torch.empty(max(16, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
@@ -309,14 +323,19 @@ def main() -> int:
             plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dt, args.config)
         flops = workload_flops(w)
         nbytes = algorithmic_bytes(w)
-        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan, split=split, ws=ws, dt=dt,
+        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan, split=split, ws=ws, dt=dt, paged=paged,
                          flops=flops, bytes=nbytes, hbm_bound=flops / nbytes < RIDGE))
 
     def launch(r):
         # the current stream is torch's capture stream while a graph is recorded
         w = r["w"]
         s = torch.cuda.current_stream(dev).cuda_stream
-        if r["split"]:
+        if r["paged"]:
+            pg = r["paged"]
+            fa.attn_fwd_paged_ex(r["q"], r["k"], r["v"], pg["bt"], pg["sl"], r["o"], r["lse"], w.B, w.Hq, w.Hkv,
+                                 w.N, w.d, pg["ps"], pg["num_pages"], pg["max_pages"], w.nk, w.causal, w.window,
+                                 w.scale, r["dt"], args.splits, args.config, r["ws"], r["ws"].numel(), s)
+        elif r["split"]:
             fa.attn_fwd_splitkv_ex(r["q"], r["k"], r["v"], r["o"], r["lse"], w.B, w.Hq, w.Hkv, w.N, w.nk, w.d,
                                    w.causal, w.window, w.scale, r["dt"], args.splits, args.config, r["ws"],
                                    r["ws"].numel(), s)
@@ -385,10 +404,13 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": runs[dom]["flops"] / (per_kernel_ms[dom] * 1e-3) / 1e12,
                 "peak": peak, "unit": "TFLOP/s"}
+    def label(r):
+        return r["w"].label() + (f"_paged{r['paged']['ps']}" if r["paged"] else "")
+
     kernels = []
     for j, r in enumerate(runs):
         t = per_kernel_ms[j] * 1e-3
-        kernels.append({"variant": r["w"].label(), "ms": round(per_kernel_ms[j], 5),
+        kernels.append({"variant": label(r), "ms": round(per_kernel_ms[j], 5),
                         "tflops": round(r["flops"] / t / 1e12, 2),
                         "frac_of_peak": round(r["flops"] / t / 1e12 / peak, 4),
                         "hbm_gbs": round(r["bytes"] / t / 1e9, 1),
@@ -411,19 +433,20 @@ def main() -> int:
         "data": "synthetic (seeded iid N(0,1) inputs, rounded to the 16-bit dtype)",
         "config": {
             "workload": args.workload,
-            "variants": [w.label() for w in wls],
+            "variants": [label(r) for r in runs],
             "parallelism": "single GPU",
             "tile_config": args.config,
             "split_kv": any(r["split"] for r in runs),
+            "paged_page_size": args.paged or None,
         },
         "roofline": {
             "bound": roof["bound"],
-            "kernel": dw.label(),
+            "kernel": label(runs[dom]),
             "achieved": round(roof["achieved"], 2),
             "peak": roof["peak"],
             "unit": roof["unit"],
             "frac": round(roof["achieved"] / roof["peak"], 4),
-            "traffic": traffic_from_profiles(dw.label()),
+            "traffic": traffic_from_profiles(label(runs[dom])),
             **({"algorithmic_bytes": roof["algorithmic_bytes"]} if "algorithmic_bytes" in roof else {}),
         },
         "kernels": kernels,

@@ -18,6 +18,11 @@ Split-KV ("Optimizaciones de Atencion", section "FlashDecoding"):
 ``attn_fwd_splitkv_plan``, ``attn_fwd_splitkv_workspace_size`` and the
 convenience ``flash_attn_forward_splitkv(q, k, v, causal=True)`` for Nq
 queries against Nk keys (decoding).
+
+Paged K/V ("00 - Por que la atencion domina la inferencia", section
+"PagedAttention es un problema distinto"): ``attn_fwd_paged``,
+``attn_fwd_paged_ex``, ``attn_fwd_paged_validate``, ``attn_fwd_paged_plan``,
+``attn_fwd_paged_workspace_size`` and ``flash_attn_forward_paged``.
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
@@ -28,6 +33,11 @@ from ._binding import (  # noqa: F401
     attn_fwd_config_desc,
     attn_fwd_ex,
     attn_fwd_num_configs,
+    attn_fwd_paged,
+    attn_fwd_paged_ex,
+    attn_fwd_paged_plan,
+    attn_fwd_paged_validate,
+    attn_fwd_paged_workspace_size,
     attn_fwd_plan,
     attn_fwd_plan_ex,
     attn_fwd_splitkv,
@@ -38,6 +48,7 @@ from ._binding import (  # noqa: F401
     attn_fwd_validate,
     attn_status_str,
     flash_attn_forward,
+    flash_attn_forward_paged,
     flash_attn_forward_splitkv,
     library_path,
     load_library,

@@ -70,6 +70,18 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_splitkv_plan.restype = cint
     lib.attn_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, cint, i64, cint, i64, cint]
     lib.attn_fwd_splitkv_workspace_size.restype = i64
+    pg = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, i64, f32, cint, i64]
+    lib.attn_fwd_paged.argtypes = pg + [vp, i64, vp]
+    lib.attn_fwd_paged.restype = cint
+    lib.attn_fwd_paged_ex.argtypes = pg + [cint, vp, i64, vp]
+    lib.attn_fwd_paged_ex.restype = cint
+    lib.attn_fwd_paged_validate.argtypes = pg + [cint, vp, i64]
+    lib.attn_fwd_paged_validate.restype = cint
+    geo = [i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, i64, cint, i64, cint]
+    lib.attn_fwd_paged_plan.argtypes = geo + [i64p]
+    lib.attn_fwd_paged_plan.restype = cint
+    lib.attn_fwd_paged_workspace_size.argtypes = geo
+    lib.attn_fwd_paged_workspace_size.restype = i64
     _lib = lib
     return lib
 
@@ -276,4 +288,116 @@ def flash_attn_forward_splitkv(q, k, v, causal: bool = True, window: int = 0, sc
         attn_fwd_splitkv_ex(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
                             num_splits, config_id, workspace, ws_bytes,
                             torch.cuda.current_stream(q.device).cuda_stream)
+    return out, lse
+
+
+# ---- paged K/V: pools (num_pages, Hkv, page_size, d), a block table per
+# request and per-request lengths
+
+_PLAN_KEYS = ("block_m", "block_n", "waves", "grid", "n_splits", "split_tiles", "config_id", "workspace_bytes",
+              "stacked")
+
+
+def attn_fwd_paged_plan(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages, max_seq_len, causal, window, dtype,
+                        num_splits=0, config_id=-1) -> dict:
+    out = (ctypes.c_int64 * 9)()
+    rc = load_library().attn_fwd_paged_plan(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages, max_seq_len,
+                                            int(causal), window, dtype, num_splits, config_id, out)
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_paged_plan")
+    return dict(zip(_PLAN_KEYS, list(out)))
+
+
+def attn_fwd_paged_workspace_size(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages, max_seq_len, causal,
+                                  window, dtype, num_splits=0, config_id=-1) -> int:
+    n = int(load_library().attn_fwd_paged_workspace_size(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages,
+                                                         max_seq_len, int(causal), window, dtype, num_splits,
+                                                         config_id))
+    if n < 0:
+        raise AttnError(-n, "attn_fwd_paged_workspace_size")
+    return n
+
+
+def attn_fwd_paged_validate(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, Nq, d, page_size,
+                            num_pages, max_pages, max_seq_len, causal, window, scale, dtype, num_splits=0,
+                            config_id=-1, workspace=None, workspace_bytes=0) -> int:
+    return load_library().attn_fwd_paged_validate(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+        Nq, d, page_size, num_pages, max_pages, max_seq_len, int(causal), window, scale, dtype, num_splits,
+        config_id, _ptr(workspace), workspace_bytes)
+
+
+def attn_fwd_paged_ex(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, Nq, d, page_size, num_pages,
+                      max_pages, max_seq_len, causal, window, scale, dtype, num_splits=0, config_id=-1,
+                      workspace=None, workspace_bytes=0, stream=None) -> None:
+    """Enqueue the paged forward; raises AttnError."""
+    rc = load_library().attn_fwd_paged_ex(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+        Nq, d, page_size, num_pages, max_pages, max_seq_len, int(causal), window, scale, dtype, num_splits,
+        config_id, _ptr(workspace), workspace_bytes, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_paged_ex")
+
+
+def attn_fwd_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, Nq, d, page_size, num_pages,
+                   max_pages, max_seq_len, causal, window, scale, dtype, num_splits=0, workspace=None,
+                   workspace_bytes=0, stream=None) -> None:
+    """Enqueue the paged forward with the automatic tile choice."""
+    rc = load_library().attn_fwd_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+        Nq, d, page_size, num_pages, max_pages, max_seq_len, int(causal), window, scale, dtype, num_splits,
+        _ptr(workspace), workspace_bytes, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_paged")
+
+
+def flash_attn_forward_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int | None = None,
+                             causal: bool = True, window: int = 0, scale: float | None = None, num_splits: int = 0,
+                             config_id: int = -1, workspace=None, out=None, lse=None, return_lse: bool = True):
+    """(B, Hq, Nq, d) queries against paged K/V: pools (num_pages, Hkv,
+    page_size, d), block_table (B, max_pages) and seq_lens (B,) int32, all
+    CUDA tensors -> (o, lse).  max_seq_len defaults to max_pages * page_size
+    (it bounds every seq_lens entry); the workspace is allocated with torch
+    when not given."""
+    import torch
+
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D, got shape {tuple(t.shape)}")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32:
+            raise TypeError(f"{name} must be an int32 CUDA tensor")
+    if not (q.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("q and the pools must share one dtype")
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_pool.shape
+    if dk != d or block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("inconsistent paged shapes")
+    max_pages = block_table.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_pages * page_size
+    q, k_pool, v_pool = q.contiguous(), k_pool.contiguous(), v_pool.contiguous()
+    block_table, seq_lens = block_table.contiguous(), seq_lens.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dtype = ATTN_F16 if q.dtype == torch.float16 else ATTN_BF16
+    need = attn_fwd_paged_workspace_size(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages, max_seq_len, causal,
+                                         window, dtype, num_splits, config_id)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        attn_fwd_paged_ex(q, k_pool, v_pool, block_table, seq_lens, out, lse, B, Hq, Hkv, Nq, d, page_size,
+                          num_pages, max_pages, max_seq_len, causal, window, scale, dtype, num_splits, config_id,
+                          workspace, ws_bytes, torch.cuda.current_stream(q.device).cuda_stream)
     return out, lse

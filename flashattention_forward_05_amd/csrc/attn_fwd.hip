@@ -223,6 +223,13 @@ Params make_params(const void *q, const void *k, const void *v, void *o, float *
     p.split_t0 = 0;
     p.ws_o = nullptr;
     p.ws_ml = nullptr;
+    p.block_table = nullptr;
+    p.seq_lens = nullptr;
+    p.paged = 0;
+    p.page_shift = 0;
+    p.max_pages = 0;
+    p.num_pages = 0;
+    p.Hkv = (int)Hkv;
     p.group = (int)(Hq / Hkv);
     p.window = mask == attnfwd::MASK_WINDOW ? (int)std::min<int64_t>(window, Nk) : 0;
     p.n_qtiles = (int)ntiles;
@@ -560,6 +567,159 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
         err = launch_merge(d, dtype, mp, (hipStream_t)stream);
     }
     return status_of(err);
+}
+
+// ---- paged K/V ---------------------------------------------------------
+
+static int paged_geometry(int64_t page_size, int64_t num_pages, int64_t max_pages, int64_t max_seq_len) {
+    if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_UNSUPPORTED;
+    if (num_pages < 1 || num_pages > INT_MAX || max_pages < 1 || max_pages > INT_MAX) return ATTN_ERR_SHAPE;
+    if (max_seq_len < 1 || max_seq_len > kMaxN || max_seq_len > max_pages * page_size) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+int attn_fwd_paged_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t d, int64_t page_size,
+                        int64_t num_pages, int64_t max_pages, int64_t max_seq_len, int causal, int64_t window,
+                        int dtype, int64_t num_splits, int config_id, int64_t *plan) {
+    int rc = paged_geometry(page_size, num_pages, max_pages, max_seq_len);
+    if (rc != ATTN_OK) return rc;
+    rc = check_sizes(B, Hq, Hkv, Nq, d, causal, window, 1.0f, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+    if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    const KvView kv = kv_view(Hq, Hkv, Nq);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
+    const TileCfg &tc = tile_cfg(d, id);
+    if (tc.kind != 0) return ATTN_ERR_UNSUPPORTED;
+    // lengths differ per batch: chunks cover [0, max_seq_len)
+    const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, max_seq_len, 0, 0, 0, d, num_splits, id);
+    if (plan) {
+        plan[0] = tc.bm();
+        plan[1] = tc.bn;
+        plan[2] = tc.waves();
+        plan[3] = Nq > 0 ? sp.grid : 0;
+        plan[4] = sp.n_splits;
+        plan[5] = sp.split_tiles;
+        plan[6] = id;
+        plan[7] = Nq > 0 ? sp.ws_bytes : 0;
+        plan[8] = kv.pack_nq > 0 ? 1 : 0;
+    }
+    return ATTN_OK;
+}
+
+int64_t attn_fwd_paged_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t d, int64_t page_size,
+                                      int64_t num_pages, int64_t max_pages, int64_t max_seq_len, int causal,
+                                      int64_t window, int dtype, int64_t num_splits, int config_id) {
+    int64_t plan[9];
+    const int rc = attn_fwd_paged_plan(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages, max_seq_len, causal,
+                                       window, dtype, num_splits, config_id, plan);
+    return rc == ATTN_OK ? plan[7] : -(int64_t)rc;
+}
+
+int attn_fwd_paged_validate(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                            const int32_t *seq_lens, const void *o, const float *lse, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t Nq, int64_t d, int64_t page_size, int64_t num_pages,
+                            int64_t max_pages, int64_t max_seq_len, int causal, int64_t window, float scale,
+                            int dtype, int64_t num_splits, int config_id, const void *workspace,
+                            int64_t workspace_bytes) {
+    if (Nq > 0 && (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)) return ATTN_ERR_NULL;
+    int rc = paged_geometry(page_size, num_pages, max_pages, max_seq_len);
+    if (rc != ATTN_OK) return rc;
+    rc = check_sizes(B, Hq, Hkv, Nq, d, causal, window, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+    if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
+    int64_t plan[9];
+    rc = attn_fwd_paged_plan(B, Hq, Hkv, Nq, d, page_size, num_pages, max_pages, max_seq_len, causal, window, dtype,
+                             num_splits, config_id, plan);
+    if (rc != ATTN_OK) return rc;
+    const uintptr_t mis = (uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)o | (uintptr_t)workspace;
+    if ((mis & 15) != 0 || ((uintptr_t)lse & 3) != 0 || ((uintptr_t)block_table & 3) != 0 ||
+        ((uintptr_t)seq_lens & 3) != 0)
+        return ATTN_ERR_ALIGN;
+    if (Nq == 0) return ATTN_OK;
+    if (plan[3] > INT_MAX || (plan[4] > 1 && B * Hq * Nq > INT_MAX)) return ATTN_ERR_SHAPE;
+    if (plan[4] > 1) {
+        if (!workspace) return ATTN_ERR_NULL;
+        if (workspace_bytes < plan[7]) return ATTN_ERR_WORKSPACE;
+    }
+    const int64_t qbytes = B * Hq * Nq * d * 2;
+    const int64_t poolbytes = num_pages * Hkv * page_size * d * 2;
+    const int64_t btbytes = B * max_pages * 4;
+    const int64_t slbytes = B * 4;
+    const int64_t lbytes = B * Hq * Nq * 4;
+    const void *ins[5] = {q, k_pool, v_pool, block_table, seq_lens};
+    const int64_t insz[5] = {qbytes, poolbytes, poolbytes, btbytes, slbytes};
+    for (int i = 0; i < 5; ++i) {
+        if (ranges_overlap(o, qbytes, ins[i], insz[i])) return ATTN_ERR_ALIAS;
+        if (lse && ranges_overlap(lse, lbytes, ins[i], insz[i])) return ATTN_ERR_ALIAS;
+        if (plan[4] > 1 && ranges_overlap(workspace, plan[7], ins[i], insz[i])) return ATTN_ERR_ALIAS;
+    }
+    if (lse && ranges_overlap(lse, lbytes, o, qbytes)) return ATTN_ERR_ALIAS;
+    if (plan[4] > 1 && (ranges_overlap(workspace, plan[7], o, qbytes) ||
+                        (lse && ranges_overlap(workspace, plan[7], lse, lbytes))))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+int attn_fwd_paged_ex(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                      const int32_t *seq_lens, void *o, float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                      int64_t d, int64_t page_size, int64_t num_pages, int64_t max_pages, int64_t max_seq_len,
+                      int causal, int64_t window, float scale, int dtype, int64_t num_splits, int config_id,
+                      void *workspace, int64_t workspace_bytes, void *stream) {
+    const int rc = attn_fwd_paged_validate(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, Nq, d,
+                                           page_size, num_pages, max_pages, max_seq_len, causal, window, scale,
+                                           dtype, num_splits, config_id, workspace, workspace_bytes);
+    if (rc != ATTN_OK) return rc;
+    if (Nq == 0) return ATTN_OK;
+    const int mask = mask_mode(causal, window);
+    const KvView kv = kv_view(Hq, Hkv, Nq);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask);
+    const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, max_seq_len, 0, 0, 0, d, num_splits, id);
+    Params p = make_params(q, k_pool, v_pool, o, lse, B, kv.Hq, kv.pack_nq > 0 ? kv.Hq : Hkv, kv.Nq, max_seq_len,
+                           window, mask, scale, sp.ntiles);
+    p.q_off = (int)(max_seq_len - Nq);   // replaced per batch from seq_lens in the kernel
+    p.pack_nq = kv.pack_nq;
+    p.zigzag = (id == 7) ? 1 : 0;
+    p.n_splits = (int)sp.n_splits;
+    p.split_tiles = (int)sp.split_tiles;
+    p.split_t0 = 0;
+    p.paged = 1;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    int shift = 0;
+    while ((int64_t(1) << shift) < page_size) ++shift;
+    p.page_shift = shift;
+    p.max_pages = (int)max_pages;
+    p.num_pages = (int)num_pages;
+    p.Hkv = (int)Hkv;
+    const int64_t rows = B * Hq * Nq;
+    if (sp.n_splits > 1) {
+        p.ws_o = (float *)workspace;
+        p.ws_ml = (float *)workspace + sp.n_splits * rows * d;
+    }
+    hipError_t err = launch(d, dtype, mask, id, p, sp.grid, (hipStream_t)stream);
+    if (err == hipSuccess && sp.n_splits > 1) {
+        attnfwd::MergeParams mp;
+        mp.ws_o = p.ws_o;
+        mp.ws_ml = p.ws_ml;
+        mp.o = (uint16_t *)o;
+        mp.lse = lse;
+        mp.rows = rows;
+        mp.n_splits = (int)sp.n_splits;
+        err = launch_merge(d, dtype, mp, (hipStream_t)stream);
+    }
+    return status_of(err);
+}
+
+int attn_fwd_paged(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                   const int32_t *seq_lens, void *o, float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                   int64_t d, int64_t page_size, int64_t num_pages, int64_t max_pages, int64_t max_seq_len,
+                   int causal, int64_t window, float scale, int dtype, int64_t num_splits, void *workspace,
+                   int64_t workspace_bytes, void *stream) {
+    return attn_fwd_paged_ex(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, Nq, d, page_size,
+                             num_pages, max_pages, max_seq_len, causal, window, scale, dtype, num_splits, -1,
+                             workspace, workspace_bytes, stream);
 }
 
 int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,

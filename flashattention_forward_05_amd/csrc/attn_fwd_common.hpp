@@ -44,6 +44,16 @@ struct Params {
     int split_t0;        // first key tile of split 0 (the first tile any query row sees)
     float *ws_o;         // n_splits > 1: partial outputs (n_splits, B*Hq, N, d), O/l in fp32
     float *ws_ml;        // n_splits > 1: partial log2-sum-exp (n_splits, B*Hq, N), m + log2 l
+    // paged K/V (paged = 1): k and v are page pools (num_pages, Hkv, page_size, d);
+    // key j of batch b lives in page block_table[b * max_pages + j / page_size] at
+    // slot j % page_size; batch b has min(seq_lens[b], Nk) keys
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int paged;
+    int page_shift;      // log2(page_size), page_size >= 8
+    int max_pages;       // block-table entries per batch
+    int num_pages;       // pages in each pool (page ids are clamped to it)
+    int Hkv;
     int group;           // Hq / Hkv
     int window;          // > 0 only with MASK_WINDOW
     int n_qtiles;        // ceil(N / BM)

@@ -88,8 +88,14 @@ struct Kernel {
     struct Ctx {
         const uint16_t *kp, *vp;
         int Nq, Nk, window, lane, g, l32, wave_q, kgroup;
-        int qw0, pw0, w_last;
+        int qw0, pw0, w_last, q_off;
         int lpos[QB];
+        // paged K/V: this batch's block-table row, the K/V head and the page geometry
+        const int32_t *bt;
+        int64_t kvh;
+        int page_shift, num_pages, Hkv;
+        int max_pages;
+        bool paged;
         float c;
         char *kst[NSTAGE];
         char *vst[NSTAGE];
@@ -98,23 +104,92 @@ struct Kernel {
     // Sequence position of query row r, and the lowest / highest position
     // over rows a .. b (a <= b): with stacked heads the rows of one range can
     // wrap from one query head to the next.
-    static __device__ __forceinline__ int pos_of(const Params &p, int r) {
-        return p.q_off + (p.pack_nq > 0 ? r % p.pack_nq : r);
+    static __device__ __forceinline__ int pos_of(const Params &p, int q_off, int r) {
+        return q_off + (p.pack_nq > 0 ? r % p.pack_nq : r);
     }
-    static __device__ __forceinline__ void pos_range(const Params &p, int a, int b, int &lo, int &hi) {
+    static __device__ __forceinline__ void pos_range(const Params &p, int q_off, int a, int b, int &lo, int &hi) {
         b = max(a, b);
         if (p.pack_nq > 0 && (b - a + 1 >= p.pack_nq || a / p.pack_nq != b / p.pack_nq)) {
-            lo = p.q_off;
-            hi = p.q_off + p.pack_nq - 1;
+            lo = q_off;
+            hi = q_off + p.pack_nq - 1;
         } else {
-            lo = pos_of(p, a);
-            hi = pos_of(p, b);
+            lo = pos_of(p, q_off, a);
+            hi = pos_of(p, q_off, b);
         }
     }
 
+    // Paged K/V: one direct-load instruction covers 64 / CHUNKS_PER_ROW (4 or
+    // 8) consecutive rows starting at a multiple of that count, so with pages
+    // of at least 8 keys its rows share one page and the page id is a scalar
+    // (a scalar-cache read of the block table: it does not count against the
+    // vector-memory waits that track the tile loads).  Rows at or past the
+    // batch's length read the last key instead (in the same page, or the last
+    // key's page when the whole group is past it), so masked rows still hold
+    // finite data.  paged_page gives the (clamped) page id of a group,
+    // paged_slot the slot of a lane's key in it.
+    static __device__ __forceinline__ int paged_page(const Ctx &x, int row_first) {
+        const int prow = __builtin_amdgcn_readfirstlane(min(row_first, x.Nk - 1));
+        const int page = ((const __attribute__((address_space(4))) int32_t *)x.bt)[prow >> x.page_shift];
+        return min(max(page, 0), x.num_pages - 1);
+    }
+    static __device__ __forceinline__ int paged_slot(const Ctx &x, int row) {
+        return min(row, x.Nk - 1) & ((1 << x.page_shift) - 1);
+    }
+
     // Issue the direct loads of tile t (keys t*BN ..) into ring stage dst.
+    // Paged tile loads with PPT consecutive block-table entries per tile
+    // (page_size = BN / PPT, or PPT = 1 when a page holds the whole tile):
+    // when the tile's entries lie inside the batch's table row they are read
+    // with one wide scalar load; group i then takes entry
+    // min(its first row, last key) / page_size of that window.  Otherwise
+    // (the last entries of a row) each group reads its own entry.
+    template <int PPT>
+    static __device__ __forceinline__ void load_tile_paged(const Ctx &x, int j0, char *kdst, char *vdst) {
+        const int e_first = j0 >> x.page_shift;
+        const int e_last = (x.Nk - 1) >> x.page_shift;
+        int page[LOADS];
+        if (e_first + PPT <= x.max_pages) {
+            int pw[PPT];
+            const __attribute__((address_space(4))) int32_t *bt =
+                (const __attribute__((address_space(4))) int32_t *)x.bt + e_first;
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) pw[k] = min(max(bt[k], 0), x.num_pages - 1);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int e = min((j0 + ((i * NWQ + x.wave_q) * 64) / CHUNKS_PER_ROW) >> x.page_shift, e_last);
+                int pg = pw[0];
+#pragma unroll
+                for (int k = 1; k < PPT; ++k) pg = (e - e_first == k) ? pw[k] : pg;
+                page[i] = pg;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) page[i] = paged_page(x, j0 + ((i * NWQ + x.wave_q) * 64) / CHUNKS_PER_ROW);
+        }
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int slot = (i * NWQ + x.wave_q) * 64 + x.lane;
+            const int row = slot / CHUNKS_PER_ROW;
+            const int ch = (slot % CHUNKS_PER_ROW) ^ swz<D>(row);
+            const int lds_off = x.kgroup * TILEB + (i * NWQ + x.wave_q) * 1024;
+            const int64_t pbase = ((int64_t)page[i] * x.Hkv + x.kvh) << x.page_shift;   // in rows
+            const uint32_t voff = (uint32_t)(paged_slot(x, j0 + row) * (D * 2) + ch * 16);
+            lds_dma16_s(x.kp + pbase * D, voff, __builtin_amdgcn_readfirstlane(lds_addr(kdst + lds_off)));
+            lds_dma16_s(x.vp + pbase * D, voff, __builtin_amdgcn_readfirstlane(lds_addr(vdst + lds_off)));
+        }
+    }
+
     static __device__ __forceinline__ void load_tile(const Ctx &x, int t, char *kdst, char *vdst) {
         const int j0 = t * BN;
+        if (x.paged) {
+            const int ppt = BN >> x.page_shift;   // 0 when a page is longer than a tile
+            if constexpr (BN >= 64) {
+                if (ppt >= 8) return load_tile_paged<8>(x, j0, kdst, vdst);
+            }
+            if (ppt >= 4) return load_tile_paged<4>(x, j0, kdst, vdst);
+            if (ppt >= 2) return load_tile_paged<2>(x, j0, kdst, vdst);
+            return load_tile_paged<1>(x, j0, kdst, vdst);
+        }
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int slot = (i * NWQ + x.wave_q) * 64 + x.lane;
@@ -275,7 +350,7 @@ struct Kernel {
         x.g = x.lane >> 5;
         x.l32 = x.lane & 31;
         x.Nq = p.N;
-        x.Nk = p.Nk;
+        x.paged = p.paged != 0;
         x.window = p.window;
         x.c = p.c;
         for (int s = 0; s < NSTAGE; ++s) {
@@ -283,7 +358,6 @@ struct Kernel {
             x.vst[s] = vst[s];
         }
         const int N = p.N;
-        const int Nk = p.Nk;
 
         // ---- which (batch*head, key split, query tile) this workgroup owns;
         // for masked runs the heaviest query tiles (most visible keys) are
@@ -299,14 +373,32 @@ struct Kernel {
         const int hkv = p.Hq / p.group;
         const int64_t kvhead = (int64_t)b * hkv + h / p.group;
         const uint16_t *qp = p.q + (int64_t)bh * N * D;
-        x.kp = p.k + kvhead * Nk * D;
-        x.vp = p.v + kvhead * Nk * D;
+        // keys of this batch, and the position offset of its query rows
+        int Nk = p.Nk;
+        int q_off = p.q_off;
+        if (x.paged) {
+            Nk = min(max(((const __attribute__((address_space(4))) int32_t *)p.seq_lens)[b], 0), p.Nk);
+            q_off = Nk - (p.pack_nq > 0 ? p.pack_nq : N);
+            x.bt = p.block_table + (int64_t)b * p.max_pages;
+            x.kvh = h / p.group;
+            x.page_shift = p.page_shift;
+            x.num_pages = p.num_pages;
+            x.max_pages = p.max_pages;
+            x.Hkv = p.Hkv;
+            x.kp = p.k;
+            x.vp = p.v;
+        } else {
+            x.kp = p.k + kvhead * Nk * D;
+            x.vp = p.v + kvhead * Nk * D;
+        }
+        x.Nk = Nk;
+        x.q_off = q_off;
 
         const int q_tile0 = qt * BM;
         x.qw0 = q_tile0 + x.wave_q * QB * 32;
-        pos_range(p, x.qw0, min(x.qw0 + QB * 32, N) - 1, x.pw0, x.w_last);
+        pos_range(p, q_off, x.qw0, min(x.qw0 + QB * 32, N) - 1, x.pw0, x.w_last);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) x.lpos[qb] = pos_of(p, x.qw0 + qb * 32 + x.l32);
+        for (int qb = 0; qb < QB; ++qb) x.lpos[qb] = pos_of(p, q_off, x.qw0 + qb * 32 + x.l32);
 
         State st;
         // ---- Q fragments (MFMA B operand): lane holds row qw0 + 32*qb + l32,
@@ -334,14 +426,14 @@ struct Kernel {
         // ---- key tiles seen by the workgroup (within its key split), divided
         // between the key groups
         int p_first, p_last;
-        pos_range(p, q_tile0, min(q_tile0 + BM, N) - 1, p_first, p_last);
+        pos_range(p, q_off, q_tile0, min(q_tile0 + BM, N) - 1, p_first, p_last);
         int kv_lo = 0, kv_hi = Nk - 1;
         if constexpr (MASK != MASK_NONE) kv_hi = min(kv_hi, p_last);
         if constexpr (MASK == MASK_WINDOW) kv_lo = max(0, p_first - p.window + 1);
         const int s_first = p.split_t0 + split * p.split_tiles;
         const int t_begin = max(kv_lo / BN, s_first);
         const int t_last = min(kv_hi / BN, s_first + p.split_tiles - 1);
-        const int n_tiles = max(0, t_last + 1 - t_begin);
+        const int n_tiles = Nk > 0 ? max(0, t_last + 1 - t_begin) : 0;
         const int half = (n_tiles + KSPLIT - 1) / KSPLIT;
         const int my_begin = t_begin + x.kgroup * half;
         const int my_count = max(0, min(half, n_tiles - x.kgroup * half));

@@ -238,6 +238,82 @@ int attn_fwd_splitkv_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_
                           int causal, int64_t window, int dtype, int64_t num_splits, int config_id,
                           int64_t *plan);
 
+/*
+ * ---- Paged K/V forward ----------------------------------------------------
+ *
+ * The split-KV forward reading K and V through a page table, as
+ * PagedAttention does ("00 - Por que la atencion domina la inferencia",
+ * section "PagedAttention es un problema distinto": the KV cache is kept in
+ * small fixed-size blocks, e.g. 16 tokens, with one table of blocks per
+ * request, and the attention kernel follows that table instead of reading a
+ * flat K and V).  Each batch entry (request) has its own key count.
+ *
+ * Layout (row-major, contiguous, device memory):
+ *   q, o         : (B, Hq, Nq, d) elements of `dtype`
+ *   k_pool, v_pool: (num_pages, Hkv, page_size, d) elements of `dtype`
+ *   block_table  : (B, max_pages) int32; entry [b][p] is the pool page that
+ *                  holds keys p*page_size .. p*page_size + page_size - 1 of
+ *                  request b (the same page index in k_pool and v_pool)
+ *   seq_lens     : (B,) int32, keys of request b (its cached tokens, the Nq
+ *                  new ones included)
+ *   lse          : (B, Hq, Nq) float32, may be NULL
+ * Key j of request b, K/V head hk, is k_pool[block_table[b][j / page_size]]
+ * [hk][j % page_size][:].  Query row i of request b sits at position
+ * seq_lens[b] - Nq + i (bottom-right alignment, as for attn_fwd_splitkv);
+ * visibility follows the split-KV rules with Nk = seq_lens[b].
+ *
+ * The device data is not checked on the host: the kernel clamps seq_lens[b]
+ * into [0, max_seq_len] and every page index into [0, num_pages), so a bad
+ * table reads wrong pages but never leaves the pools.  Block-table entries
+ * past ceil(seq_lens[b] / page_size) are not read.  A query row whose
+ * position is negative (seq_lens[b] < Nq with causal) sees no key: its output
+ * is 0 and its log-sum-exp -inf.  Slots of a page past seq_lens[b] are never
+ * read.
+ *
+ * page_size: a power of two, 8 .. 256.  max_seq_len: an upper bound of every
+ * seq_lens[b], at most max_pages * page_size; the work is split over
+ * [0, max_seq_len).  Workspace, num_splits and the rest: as attn_fwd_splitkv
+ * (num_splits = 0 is automatic).  Errors: those of attn_fwd_splitkv, plus
+ * ATTN_ERR_NULL for a NULL k_pool, v_pool, block_table or seq_lens,
+ * ATTN_ERR_UNSUPPORTED for a page_size that is not a power of two in
+ * [8, 256], ATTN_ERR_SHAPE for num_pages or max_pages < 1 or max_seq_len
+ * outside [1, max_pages * page_size], ATTN_ERR_ALIGN for a block_table or
+ * seq_lens not 4-byte aligned, ATTN_ERR_ALIAS when o, lse or the workspace
+ * overlaps the pools, the table or the lengths.
+ */
+int attn_fwd_paged(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                   const int32_t *seq_lens, void *o, float *lse, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t Nq, int64_t d, int64_t page_size, int64_t num_pages, int64_t max_pages,
+                   int64_t max_seq_len, int causal, int64_t window, float scale, int dtype,
+                   int64_t num_splits, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* attn_fwd_paged with an explicit tile configuration (-1 = automatic). */
+int attn_fwd_paged_ex(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                      const int32_t *seq_lens, void *o, float *lse, int64_t B, int64_t Hq, int64_t Hkv,
+                      int64_t Nq, int64_t d, int64_t page_size, int64_t num_pages, int64_t max_pages,
+                      int64_t max_seq_len, int causal, int64_t window, float scale, int dtype,
+                      int64_t num_splits, int config_id, void *workspace, int64_t workspace_bytes,
+                      void *stream);
+
+/* The host-side checks of attn_fwd_paged_ex alone. */
+int attn_fwd_paged_validate(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                            const int32_t *seq_lens, const void *o, const float *lse, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t Nq, int64_t d, int64_t page_size, int64_t num_pages,
+                            int64_t max_pages, int64_t max_seq_len, int causal, int64_t window, float scale,
+                            int dtype, int64_t num_splits, int config_id, const void *workspace,
+                            int64_t workspace_bytes);
+
+/* The plan of a paged call, the 9 integers of attn_fwd_splitkv_plan. */
+int attn_fwd_paged_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t d, int64_t page_size,
+                        int64_t num_pages, int64_t max_pages, int64_t max_seq_len, int causal, int64_t window,
+                        int dtype, int64_t num_splits, int config_id, int64_t *plan);
+
+/* Workspace bytes of a paged call (0 with one chunk), or minus the status. */
+int64_t attn_fwd_paged_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t d,
+                                      int64_t page_size, int64_t num_pages, int64_t max_pages,
+                                      int64_t max_seq_len, int causal, int64_t window, int dtype,
+                                      int64_t num_splits, int config_id);
+
 #ifdef __cplusplus
 }
 #endif

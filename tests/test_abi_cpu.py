@@ -202,3 +202,43 @@ def test_splitkv_plan_and_workspace():
     assert fa.load_library().attn_fwd_splitkv_workspace_size(1, 3, 2, 1, 10, 64, 1, 0, 0, 0, -1) == -2
     with pytest.raises(fa.AttnError):
         fa.attn_fwd_splitkv_plan(1, 1, 1, 8, 4, 64, 1, 0, 0)    # causal with Nq > Nk
+
+
+# ---- paged K/V entry points (host checks, plan)
+PG = dict(q=G, kp=2 * G, vp=3 * G, bt=4 * G, sl=4 * G + (1 << 20), o=5 * G, lse=6 * G, B=2, Hq=8, Hkv=2, Nq=1,
+          d=128, page_size=16, num_pages=1000, max_pages=256, max_seq_len=4096, causal=1, window=0, scale=0.1,
+          dtype=1, num_splits=0, config_id=-1, workspace=7 * G, workspace_bytes=1 << 20)
+
+
+def validate_pg(**over):
+    a = dict(PG, **over)
+    return fa.attn_fwd_paged_validate(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["o"], a["lse"], a["B"],
+                                      a["Hq"], a["Hkv"], a["Nq"], a["d"], a["page_size"], a["num_pages"],
+                                      a["max_pages"], a["max_seq_len"], a["causal"], a["window"], a["scale"],
+                                      a["dtype"], a["num_splits"], a["config_id"], a["workspace"],
+                                      a["workspace_bytes"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, 0), ({"lse": None}, 0), ({"page_size": 8, "max_pages": 512}, 0), ({"page_size": 256, "max_pages": 16}, 0),
+    ({"Nq": 0, "q": None, "kp": None, "vp": None, "bt": None, "sl": None, "o": None}, 0),
+    ({"bt": None}, 1), ({"sl": None}, 1), ({"kp": None}, 1), ({"workspace": None}, 1),
+    ({"max_seq_len": 4097}, 2), ({"max_seq_len": 0}, 2), ({"num_pages": 0}, 2), ({"max_pages": 0}, 2),
+    ({"page_size": 4}, 3), ({"page_size": 24}, 3), ({"page_size": 512, "max_pages": 8}, 3), ({"d": 96}, 3),
+    ({"config_id": 6}, 3),
+    ({"num_splits": -1}, 4),
+    ({"bt": 4 * G + 2}, 5), ({"sl": 4 * G + (1 << 20) + 1}, 5), ({"workspace": 7 * G + 4}, 5),
+    ({"o": 2 * G + 64}, 6), ({"lse": 4 * G}, 6), ({"workspace": 3 * G}, 6), ({"workspace": 4 * G + (1 << 20)}, 6),
+    ({"workspace_bytes": 16}, 9),
+])
+def test_paged_validate_codes(over, code):
+    assert validate_pg(**over) == code
+
+
+def test_paged_plan():
+    p = fa.attn_fwd_paged_plan(4, 32, 8, 1, 128, 16, 3000, 512, 8192, 1, 0, 1)
+    s = fa.attn_fwd_splitkv_plan(4, 32, 8, 1, 8192, 128, 1, 0, 1)
+    assert p == s                       # same plan as the contiguous call of the same maximum length
+    assert fa.attn_fwd_paged_workspace_size(4, 32, 8, 1, 128, 16, 3000, 512, 8192, 1, 0, 1) == p["workspace_bytes"]
+    w = fa.attn_fwd_paged_plan(1, 32, 1, 1, 128, 16, 3000, 2048, 32768, 1, 4096, 1)
+    assert w["n_splits"] * w["split_tiles"] >= 32768 // w["block_n"]   # lengths vary: chunks span all keys
