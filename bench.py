@@ -232,6 +232,8 @@ def main() -> int:
     ap.add_argument("--splitkv", action="store_true",
                     help="run every variant through the split-KV entry point (decoding workloads always are)")
     ap.add_argument("--splits", type=int, default=0, help="key chunks for split-KV calls (0: automatic)")
+    ap.add_argument("--tune", action="store_true",
+                    help="before timing, pick each (non-split) variant's tile configuration with attn_fwd_autotune")
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="keep the K/V of decoding workloads in pages of this many tokens (random page order) "
                          "and run the paged entry point")
@@ -323,7 +325,13 @@ def main() -> int:
             plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dt, args.config)
         flops = workload_flops(w)
         nbytes = algorithmic_bytes(w)
-        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan, split=split, ws=ws, dt=dt, paged=paged,
+        cfg = args.config
+        if args.tune and not split and not paged:
+            cfg, tms = fa.attn_fwd_autotune(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
+                                            w.scale, dt, reps=10)
+            plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dt, cfg)
+            plan["tuning_ms"] = {str(i): round(t, 5) for i, t in tms.items()}
+        runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan, split=split, ws=ws, dt=dt, paged=paged, cfg=cfg,
                          flops=flops, bytes=nbytes, hbm_bound=flops / nbytes < RIDGE))
 
     def launch(r):
@@ -341,7 +349,7 @@ def main() -> int:
                                    r["ws"].numel(), s)
         else:
             fa.attn_fwd_ex(r["q"], r["k"], r["v"], r["o"], r["lse"], w.B, w.Hq, w.Hkv, w.N, w.d,
-                           w.causal, w.window, w.scale, r["dt"], args.config, s)
+                           w.causal, w.window, w.scale, r["dt"], r["cfg"], s)
 
     for r in runs:                       # eager warm-up (also checks every launch)
         launch(r)
@@ -435,7 +443,7 @@ def main() -> int:
             "workload": args.workload,
             "variants": [label(r) for r in runs],
             "parallelism": "single GPU",
-            "tile_config": args.config,
+            "tile_config": "tuned" if args.tune else args.config,
             "split_kv": any(r["split"] for r in runs),
             "paged_page_size": args.paged or None,
         },

@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     STATUS,
     AttnError,
     attn_fwd,
+    attn_fwd_autotune,
     attn_fwd_config_desc,
     attn_fwd_ex,
     attn_fwd_num_configs,
@@ -52,4 +53,5 @@ from ._binding import (  # noqa: F401
     flash_attn_forward_splitkv,
     library_path,
     load_library,
+    tuned_configs,
 )

@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_splitkv_plan.restype = cint
     lib.attn_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, cint, i64, cint, i64, cint]
     lib.attn_fwd_splitkv_workspace_size.restype = i64
+    lib.attn_fwd_autotune.argtypes = common + [cint, ctypes.POINTER(cint), ctypes.POINTER(f32), vp]
+    lib.attn_fwd_autotune.restype = cint
     pg = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, i64, f32, cint, i64]
     lib.attn_fwd_paged.argtypes = pg + [vp, i64, vp]
     lib.attn_fwd_paged.restype = cint
@@ -162,10 +164,38 @@ def attn_fwd_config_desc(config_id: int, d: int = 64) -> dict:
     return dict(zip(keys, list(out)))
 
 
+def attn_fwd_autotune(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, reps=20,
+                      stream=None) -> tuple[int, dict]:
+    """Time every built tile configuration on these buffers (synchronises the
+    stream); returns (fastest id, {id: ms per call})."""
+    best = ctypes.c_int(-1)
+    n = attn_fwd_num_configs()
+    ms = (ctypes.c_float * n)()
+    rc = load_library().attn_fwd_autotune(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                          int(causal), window, scale, dtype, reps, ctypes.byref(best), ms,
+                                          _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_autotune")
+    return best.value, {i: float(ms[i]) for i in range(n) if ms[i] >= 0.0}
+
+
+# configuration picked by attn_fwd_autotune per (shape, dtype, mask, device),
+# filled by flash_attn_forward(..., tune=True)
+_TUNED: dict = {}
+
+
+def tuned_configs() -> dict:
+    """The per-shape tuning results of this process (a copy)."""
+    return dict(_TUNED)
+
+
 def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None,
-                       config_id: int = -1, out=None, lse=None, return_lse: bool = True):
+                       config_id: int = -1, out=None, lse=None, return_lse: bool = True, tune: bool = False):
     """(B, Hq, N, d) query, (B, Hkv, N, d) key/value fp16 or bf16 CUDA tensors
-    -> (o, lse).  scale defaults to 1/sqrt(d).  Inputs are made contiguous."""
+    -> (o, lse).  scale defaults to 1/sqrt(d).  Inputs are made contiguous.
+    With tune=True the first call of a shape times every tile configuration on
+    it (attn_fwd_autotune, which synchronises) and later calls of that shape
+    use the fastest."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -192,8 +222,14 @@ def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: flo
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     dtype = ATTN_F16 if q.dtype == torch.float16 else ATTN_BF16
     with torch.cuda.device(q.device):
-        attn_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, config_id,
-                    torch.cuda.current_stream(q.device).cuda_stream)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        if tune and config_id == -1:
+            key = (q.device.index, B, Hq, Hkv, N, d, dtype, bool(causal), int(window))
+            if key not in _TUNED:
+                _TUNED[key] = attn_fwd_autotune(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale,
+                                                dtype, reps=10, stream=stream)[0]
+            config_id = _TUNED[key]
+        attn_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, config_id, stream)
     return out, lse
 
 

@@ -14,6 +14,9 @@ LIB_PATH = os.path.join(LIB_DIR, "libattn_fwd.so")
 # (source, extra flags): the pipelined kernels keep MFMA results in VGPRs
 SOURCES = [
     (os.path.join(CSRC, "attn_fwd.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
+    (os.path.join(CSRC, "attn_fwd_d128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
+    (os.path.join(CSRC, "attn_fwd_paged64.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
+    (os.path.join(CSRC, "attn_fwd_paged128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_pipe.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Rpass-analysis=kernel-resource-usage"]),
 ]
 # Kernels whose loads are tracked by explicit vmcnt waits must not touch
@@ -21,7 +24,7 @@ SOURCES = [
 NO_SCRATCH = ("attn_fwd_pipe_kernel", "attn_fwd_kernel", "attn_fwd_pingpong_kernel")
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp", "attn_fwd_pingpong.hpp",
                                             "attn_fwd_pipe.hpp", "attn_fwd_launch.hpp",
-                                            "attn_fwd_merge.hpp")] + [
+                                            "attn_fwd_merge.hpp", "attn_fwd_lockstep.hpp")] + [
     os.path.join(INCLUDE, "attn_fwd.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -9,8 +9,8 @@
 #include <cstdint>
 
 #include "attn_fwd.h"
-#include "attn_fwd_kernel.hpp"
 #include "attn_fwd_launch.hpp"
+#include "attn_fwd_lockstep.hpp"
 #include "attn_fwd_merge.hpp"
 #include "attn_fwd_pingpong.hpp"
 
@@ -104,14 +104,6 @@ int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask) {
     return wg128 < 128 ? 7 : 1;
 }
 
-template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
-hipError_t launch_one(const Params &p, int64_t grid, hipStream_t stream) {
-    Params args = p;
-    void *argv[] = {&args};
-    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_kernel<D, DT, MASK, QB, NWQ, KSPLIT, BN, NSTAGE>,
-                           dim3((unsigned)grid), dim3(NWQ * KSPLIT * 64), argv, 0, stream);
-}
-
 template <int D, int DT, int MASK, int NWG, bool ROWS, int BN>
 hipError_t launch_pp(const Params &p, int64_t grid, hipStream_t stream) {
     Params args = p;
@@ -120,45 +112,39 @@ hipError_t launch_pp(const Params &p, int64_t grid, hipStream_t stream) {
                            dim3((unsigned)grid), dim3(2 * NWG * 64), argv, 0, stream);
 }
 
-template <int D, int DT, int MASK>
-hipError_t launch_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
-    constexpr bool small = D == 64;
+// d = 64, contiguous K/V: lockstep configurations here, ping-pong (4, 5; built
+// for d = 64 only: at d = 128 it does not fit its registers without
+// spilling) and pipelined (6, its own translation unit).
+template <int DT, int MASK>
+hipError_t launch_cfg64(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
     switch (cfg) {
-    case 0: return launch_one<D, DT, MASK, 1, 4, 1, 64, 3>(p, grid, stream);
-    case 1: return launch_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2>(p, grid, stream);
-    case 2: return launch_one<D, DT, MASK, 1, 8, 1, 64, 3>(p, grid, stream);
-    case 3: return launch_one<D, DT, MASK, 2, 4, 1, small ? 64 : 32, 3>(p, grid, stream);
-    // the ping-pong kernel is built for d = 64 only: at d = 128 it does not
-    // fit its registers without spilling
-    case 4:
-        if constexpr (small) return launch_pp<D, DT, MASK, 4, true, 64>(p, grid, stream);
-        else return hipErrorInvalidValue;
-    case 5:
-        if constexpr (small) return launch_pp<D, DT, MASK, 4, false, 64>(p, grid, stream);
-        else return hipErrorInvalidValue;
-    case 6: return attnfwd::launch_pipelined(D, DT, MASK, cfg, p, grid, stream);
-    case 7: return launch_one<D, DT, MASK, 1, 2, 2, small ? 64 : 32, 2>(p, grid, stream);
-    case 8: return launch_one<D, DT, MASK, 1, 1, 1, small ? 64 : 32, 3>(p, grid, stream);
-    default: return hipErrorInvalidValue;
+    case 4: return launch_pp<64, DT, MASK, 4, true, 64>(p, grid, stream);
+    case 5: return launch_pp<64, DT, MASK, 4, false, 64>(p, grid, stream);
+    case 6: return attnfwd::launch_pipelined(64, DT, MASK, cfg, p, grid, stream);
+    default: return attnfwd::launch_lockstep_cfg<64, DT, MASK, false>(cfg, p, grid, stream);
     }
 }
 
-template <int D, int DT>
-hipError_t launch_mask(int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream) {
+template <int DT>
+hipError_t launch_mask64(int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream) {
     switch (mask) {
-    case attnfwd::MASK_NONE: return launch_cfg<D, DT, attnfwd::MASK_NONE>(cfg, p, grid, stream);
-    case attnfwd::MASK_CAUSAL: return launch_cfg<D, DT, attnfwd::MASK_CAUSAL>(cfg, p, grid, stream);
-    default: return launch_cfg<D, DT, attnfwd::MASK_WINDOW>(cfg, p, grid, stream);
+    case attnfwd::MASK_NONE: return launch_cfg64<DT, attnfwd::MASK_NONE>(cfg, p, grid, stream);
+    case attnfwd::MASK_CAUSAL: return launch_cfg64<DT, attnfwd::MASK_CAUSAL>(cfg, p, grid, stream);
+    default: return launch_cfg64<DT, attnfwd::MASK_WINDOW>(cfg, p, grid, stream);
     }
 }
 
+// Routes a launch to the translation unit that holds its instantiation.
 hipError_t launch(int64_t d, int dtype, int mask, int cfg, const Params &p, int64_t grid,
                   hipStream_t stream) {
+    const int dt = dtype == ATTN_F16 ? 0 : 1;
+    if (p.paged)
+        return d == 64 ? attnfwd::launch_lockstep_paged64(dt, mask, cfg, p, grid, stream)
+                       : attnfwd::launch_lockstep_paged128(dt, mask, cfg, p, grid, stream);
     if (d == 64)
-        return dtype == ATTN_F16 ? launch_mask<64, 0>(mask, cfg, p, grid, stream)
-                                 : launch_mask<64, 1>(mask, cfg, p, grid, stream);
-    return dtype == ATTN_F16 ? launch_mask<128, 0>(mask, cfg, p, grid, stream)
-                             : launch_mask<128, 1>(mask, cfg, p, grid, stream);
+        return dt == 0 ? launch_mask64<0>(mask, cfg, p, grid, stream) : launch_mask64<1>(mask, cfg, p, grid, stream);
+    if (cfg == 6) return attnfwd::launch_pipelined(128, dt, mask, cfg, p, grid, stream);
+    return attnfwd::launch_lockstep_d128(dt, mask, cfg, p, grid, stream);
 }
 
 // Number of query tiles (from the first) whose first row sees fewer than
@@ -567,6 +553,53 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
         err = launch_merge(d, dtype, mp, (hipStream_t)stream);
     }
     return status_of(err);
+}
+
+// ---- tile-configuration tuning ------------------------------------------
+
+int attn_fwd_autotune(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t N, int64_t d, int causal, int64_t window, float scale, int dtype,
+                      int reps, int *best_config, float *ms, void *stream) {
+    if (!best_config) return ATTN_ERR_NULL;
+    if (reps < 1 || reps > 10000) return ATTN_ERR_ARG;
+    int rc = attn_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    *best_config = auto_config(B, Hq, N, d, mask_mode(causal, window));
+    if (ms)
+        for (int id = 0; id < kNumConfigs; ++id) ms[id] = -1.0f;
+    if (N == 0) return ATTN_OK;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return ATTN_ERR_LAUNCH;
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    float best = -1.0f;
+    rc = ATTN_OK;
+    for (int id = 0; id < kNumConfigs && rc == ATTN_OK; ++id) {
+        if (!cfg_built(d, id)) continue;
+        // one untimed call, then `reps` back-to-back calls between two events
+        rc = attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, id, stream);
+        if (rc != ATTN_OK) break;
+        if (hipEventRecord(e0, st) != hipSuccess) rc = ATTN_ERR_LAUNCH;
+        for (int r = 0; r < reps && rc == ATTN_OK; ++r)
+            rc = attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, id, stream);
+        if (rc == ATTN_OK && hipEventRecord(e1, st) != hipSuccess) rc = ATTN_ERR_LAUNCH;
+        if (rc == ATTN_OK && hipEventSynchronize(e1) != hipSuccess) rc = ATTN_ERR_LAUNCH;
+        float t = 0.0f;
+        if (rc == ATTN_OK && hipEventElapsedTime(&t, e0, e1) != hipSuccess) rc = ATTN_ERR_LAUNCH;
+        if (rc != ATTN_OK) break;
+        t /= (float)reps;
+        if (ms) ms[id] = t;
+        if (best < 0.0f || t < best) {
+            best = t;
+            *best_config = id;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return rc;
 }
 
 // ---- paged K/V ---------------------------------------------------------

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attnfwd {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -161,6 +163,29 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, ui
 #pragma clang diagnostic pop
 }
 
+// The same two loads with the LDS address given as a wave-uniform base plus
+// a compile-time byte offset, added into m0 by the load sequence itself: the
+// compiler then keeps one base per ring stage live instead of one address per
+// load slot (which otherwise runs the kernels out of scalar registers).
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_at(const void *gptr, uint32_t lds_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base), "i"(OFF)
+                 : "memory", "m0", "scc");
+#pragma clang diagnostic pop
+}
+
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_s_at(const void *sbase, uint32_t voff, uint32_t lds_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base),
+                 "i"(OFF)
+                 : "memory", "m0", "scc");
+#pragma clang diagnostic pop
+}
+
 // LDS byte address of a pointer into an LDS object.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
@@ -186,6 +211,20 @@ __device__ __forceinline__ int masked_qtile(int rank, int n, int zigzag) {
     const int h = (n + 1) / 2;
     if (!zigzag || rank < h) return n - 1 - rank;
     return rank - h;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time
+// indices for template arguments inside an unrolled loop).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_from<0, N>(f);
 }
 
 // Workgroup barrier with no memory-counter waits; the compiler may not move

@@ -1,0 +1,13 @@
+// attn_fwd_d128.hip -- lockstep kernel instantiations for contiguous K/V, head dim 128
+// (a translation unit of its own so that the library's slices compile in
+// parallel).
+#include "attn_fwd_launch.hpp"
+#include "attn_fwd_lockstep.hpp"
+
+namespace attnfwd {
+
+hipError_t launch_lockstep_d128(int dt, int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream) {
+    return launch_lockstep_d<128, false>(dt, mask, cfg, p, grid, stream);
+}
+
+}  // namespace attnfwd

@@ -55,7 +55,7 @@
 
 namespace attnfwd {
 
-template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
+template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE, bool PAGED = false>
 struct Kernel {
     static constexpr int BM = NWQ * QB * 32;
     static constexpr int NWAVES = NWQ * KSPLIT;
@@ -95,7 +95,6 @@ struct Kernel {
         int64_t kvh;
         int page_shift, num_pages, Hkv;
         int max_pages;
-        bool paged;
         float c;
         char *kst[NSTAGE];
         char *vst[NSTAGE];
@@ -166,22 +165,28 @@ struct Kernel {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) page[i] = paged_page(x, j0 + ((i * NWQ + x.wave_q) * 64) / CHUNKS_PER_ROW);
         }
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        const uint32_t kb = lds_base(x, kdst), vb = lds_base(x, vdst);
+        static_for<LOADS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
             const int slot = (i * NWQ + x.wave_q) * 64 + x.lane;
             const int row = slot / CHUNKS_PER_ROW;
             const int ch = (slot % CHUNKS_PER_ROW) ^ swz<D>(row);
-            const int lds_off = x.kgroup * TILEB + (i * NWQ + x.wave_q) * 1024;
             const int64_t pbase = ((int64_t)page[i] * x.Hkv + x.kvh) << x.page_shift;   // in rows
             const uint32_t voff = (uint32_t)(paged_slot(x, j0 + row) * (D * 2) + ch * 16);
-            lds_dma16_s(x.kp + pbase * D, voff, __builtin_amdgcn_readfirstlane(lds_addr(kdst + lds_off)));
-            lds_dma16_s(x.vp + pbase * D, voff, __builtin_amdgcn_readfirstlane(lds_addr(vdst + lds_off)));
-        }
+            lds_dma16_s_at<i * NWQ * 1024>(x.kp + pbase * D, voff, kb);
+            lds_dma16_s_at<i * NWQ * 1024>(x.vp + pbase * D, voff, vb);
+        });
+    }
+
+    // Wave-uniform LDS address of this wave's first load slot in a ring
+    // stage; slot i is at + i * NWQ * 1024.
+    static __device__ __forceinline__ uint32_t lds_base(const Ctx &x, const char *stage) {
+        return __builtin_amdgcn_readfirstlane(lds_addr(stage + x.kgroup * TILEB + x.wave_q * 1024));
     }
 
     static __device__ __forceinline__ void load_tile(const Ctx &x, int t, char *kdst, char *vdst) {
         const int j0 = t * BN;
-        if (x.paged) {
+        if constexpr (PAGED) {
             const int ppt = BN >> x.page_shift;   // 0 when a page is longer than a tile
             if constexpr (BN >= 64) {
                 if (ppt >= 8) return load_tile_paged<8>(x, j0, kdst, vdst);
@@ -190,18 +195,18 @@ struct Kernel {
             if (ppt >= 2) return load_tile_paged<2>(x, j0, kdst, vdst);
             return load_tile_paged<1>(x, j0, kdst, vdst);
         }
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        const uint32_t kb = lds_base(x, kdst), vb = lds_base(x, vdst);
+        static_for<LOADS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
             const int slot = (i * NWQ + x.wave_q) * 64 + x.lane;
             const int row = slot / CHUNKS_PER_ROW;
             const int chp = slot % CHUNKS_PER_ROW;
             const int ch = chp ^ swz<D>(row);
             const int64_t grow = min(j0 + row, x.Nk - 1);
             const int64_t off = grow * D + ch * 8;
-            const int lds_off = x.kgroup * TILEB + (i * NWQ + x.wave_q) * 1024;
-            lds_dma16(x.kp + off, __builtin_amdgcn_readfirstlane(lds_addr(kdst + lds_off)));
-            lds_dma16(x.vp + off, __builtin_amdgcn_readfirstlane(lds_addr(vdst + lds_off)));
-        }
+            lds_dma16_at<i * NWQ * 1024>(x.kp + off, kb);
+            lds_dma16_at<i * NWQ * 1024>(x.vp + off, vb);
+        });
     }
 
     // V^T A-operand fragment for 16-key step ks and channel block cb: two
@@ -350,7 +355,6 @@ struct Kernel {
         x.g = x.lane >> 5;
         x.l32 = x.lane & 31;
         x.Nq = p.N;
-        x.paged = p.paged != 0;
         x.window = p.window;
         x.c = p.c;
         for (int s = 0; s < NSTAGE; ++s) {
@@ -376,7 +380,7 @@ struct Kernel {
         // keys of this batch, and the position offset of its query rows
         int Nk = p.Nk;
         int q_off = p.q_off;
-        if (x.paged) {
+        if constexpr (PAGED) {
             Nk = min(max(((const __attribute__((address_space(4))) int32_t *)p.seq_lens)[b], 0), p.Nk);
             q_off = Nk - (p.pack_nq > 0 ? p.pack_nq : N);
             x.bt = p.block_table + (int64_t)b * p.max_pages;
@@ -563,9 +567,9 @@ struct Kernel {
 
 // Ring-stage LDS objects are declared one by one so that each stage is a
 // distinct object to the compiler's alias analysis.
-template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE>
+template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTAGE, bool PAGED = false>
 __global__ __launch_bounds__(NWQ * KSPLIT * 64) void attn_fwd_kernel(Params p) {
-    using K = Kernel<D, DT, MASK, QB, NWQ, KSPLIT, BN, NSTAGE>;
+    using K = Kernel<D, DT, MASK, QB, NWQ, KSPLIT, BN, NSTAGE, PAGED>;
     constexpr int SB = K::STAGEB;
     __shared__ __attribute__((aligned(1024))) char k0[SB];
     __shared__ __attribute__((aligned(1024))) char v0[SB];

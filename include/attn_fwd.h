@@ -146,6 +146,27 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
                 void *stream);
 
 /*
+ * Tile-configuration tuning.  "Lab 02 - Forward de flash attention en Triton",
+ * section "Restricciones", fixes the tile sizes on the first pass and leaves
+ * autotuning as the polishing step; this is that step for these kernels.
+ * Runs attn_fwd_ex on the caller's buffers with every configuration built
+ * for d: one untimed call, then `reps` (1 .. 10000) calls between two HIP
+ * events on `stream`.  Writes the fastest id to *best_config (the automatic
+ * choice when N == 0) and, when ms is not NULL, the mean milliseconds per call
+ * of each configuration to ms[0 .. attn_fwd_num_configs()-1] (-1 for ids
+ * not built for d).  o and lse are overwritten (every configuration computes
+ * the same function).  Unlike every other entry point it waits for the
+ * stream (an event synchronisation per configuration) and creates two HIP
+ * events; it allocates no device memory.  Errors: those of attn_fwd_validate,
+ * ATTN_ERR_NULL for a NULL best_config, ATTN_ERR_ARG for reps out of range,
+ * ATTN_ERR_LAUNCH when a launch or an event call fails.
+ */
+int attn_fwd_autotune(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                      int64_t window, float scale, int dtype, int reps, int *best_config, float *ms,
+                      void *stream);
+
+/*
  * ---- Split-KV forward ("FlashDecoding") ----------------------------------
  *
  * The same operation for Nq query rows against Nk keys, with the key range cut

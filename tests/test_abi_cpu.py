@@ -242,3 +242,15 @@ def test_paged_plan():
     assert fa.attn_fwd_paged_workspace_size(4, 32, 8, 1, 128, 16, 3000, 512, 8192, 1, 0, 1) == p["workspace_bytes"]
     w = fa.attn_fwd_paged_plan(1, 32, 1, 1, 128, 16, 3000, 2048, 32768, 1, 4096, 1)
     assert w["n_splits"] * w["split_tiles"] >= 32768 // w["block_n"]   # lengths vary: chunks span all keys
+
+
+def test_autotune_rejects_before_touching_the_gpu():
+    lib = fa.load_library()
+    best = ctypes.c_int(-7)
+    args = (A, 2 * A, 3 * A, 4 * A, None, 1, 1, 1, 8, 64, 0, 0, 0.1, 0)
+    assert lib.attn_fwd_autotune(*args, 10, None, None, None) == 1          # NULL best_config
+    assert lib.attn_fwd_autotune(*args, 0, ctypes.byref(best), None, None) == 4
+    assert lib.attn_fwd_autotune(*args, 10001, ctypes.byref(best), None, None) == 4
+    bad = (A, 2 * A, 3 * A, 4 * A, None, 1, 3, 2, 8, 64, 0, 0, 0.1, 0)      # Hq % Hkv != 0
+    assert lib.attn_fwd_autotune(*bad, 10, ctypes.byref(best), None, None) == 2
+    assert best.value == -7

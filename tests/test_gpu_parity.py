@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from attn_inputs import WORKLOADS, make_workload
-from gpu_helpers import (TOL_LSE, TOL_O, check, errors, inputs, need_gpu, oracle_full,
+from gpu_helpers import (DT_CODE, TOL_LSE, TOL_O, check, errors, inputs, need_gpu, oracle_full,
                          oracle_sampled, run_gpu, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
@@ -212,3 +212,27 @@ def test_flash_attn_forward_wrapper(fa):
     torch.cuda.synchronize()
     ro, rl = oracle_full(q, k, v, causal=True)
     check("wrapper", o.cpu(), lse.cpu(), ro, rl, "bf16")
+
+
+# ---- tile-configuration tuning
+@pytest.mark.parametrize("d,dt", [(64, "f16"), (128, "bf16")])
+def test_autotune(fa, d, dt):
+    import flashattention_forward_05_amd as fa_mod
+    B, H, N = 1, 4, 700
+    q, k, v = inputs(B, H, H, N, d, dt, seed=31)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    best, ms = fa_mod.attn_fwd_autotune(qd, kd, vd, o, lse, B, H, H, N, d, True, 0, d ** -0.5,
+                                        DT_CODE[dt], reps=5)
+    built = [i for i in range(fa_mod.attn_fwd_num_configs()) if not (d == 128 and i in (4, 5))]
+    assert sorted(ms) == built and best in ms and ms[best] == min(ms.values())
+    ro, rl = oracle_full(q, k, v, causal=True)
+    check(f"after tuning (last config run)", o.cpu(), lse.cpu(), ro, rl, dt)
+    # the wrapper tunes a shape once and then uses the fastest configuration
+    for _ in range(2):
+        o2, l2 = fa_mod.flash_attn_forward(qd, kd, vd, causal=True, tune=True)
+        torch.cuda.synchronize()
+        check("tuned wrapper", o2.cpu(), l2.cpu(), ro, rl, dt)
+    assert any(key[1:6] == (B, H, H, N, d) for key in fa_mod.tuned_configs())
