@@ -262,11 +262,15 @@ KvView kv_view(int64_t Hq, int64_t Hkv, int64_t Nq) {
     return {Hq, Nq, 0};
 }
 
-// Automatic choice for split-KV calls: one-wave 32-row workgroups for a few
-// query rows per (stacked) head (decoding), else the choice of the plain
-// forward.
+// Automatic choice for split-KV calls (from measurement): one-wave 32-row
+// workgroups while a (stacked) head has fewer than 32 rows (GQA decoding: few
+// rows, many K/V heads, so many workgroups); at 32 rows and more, with few
+// K/V heads (MQA decoding), the 8-wave workgroups of configuration 1 keep
+// more loads in flight per compute unit; longer query blocks take the choice
+// of the plain forward.
 int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask) {
-    if (Nq <= 32) return 8;
+    if (Nq < 32) return 8;
+    if (Nq <= 128) return 1;
     return auto_config(B, Hq, Nq, d, mask);
 }
 
