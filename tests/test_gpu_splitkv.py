@@ -149,3 +149,25 @@ def test_flash_attn_forward_splitkv_wrapper(fa):
     torch.cuda.synchronize()
     ro, rl = oracle_full(q, k, v, causal=True)
     check("wrapper", o.cpu(), lse.cpu(), ro, rl, "bf16")
+
+
+def test_splitkv_random_shapes(fa):
+    """Seeded random shapes, masks, chunk counts and configurations."""
+    rng = np.random.default_rng(1234)
+    for n in range(16):
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f16", "bf16"]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 3))
+        Nk = int(rng.integers(1, 2500))
+        Nq = int(min(Nk, rng.choice([1, 2, 5, 16, 17, 40, 100])))
+        causal = bool(rng.integers(0, 4) > 0)
+        window = int(rng.choice([0, 0, 1, 7, 300])) if causal else 0
+        splits = int(rng.choice([0, 1, 2, 5, 64]))
+        cfg = int(rng.choice([-1, 0, 1, 7, 8]))
+        q, k, v = qkv(B, G * Hkv, Hkv, Nq, Nk, d, dt, seed=100 + n)
+        ro, rl = oracle_full(q, k, v, causal=causal, window=window)
+        o, lse = run_gpu_splitkv(q, k, v, causal=causal, window=window, num_splits=splits, config_id=cfg)
+        check(f"#{n} B{B} Hq{G * Hkv}/{Hkv} Nq{Nq} Nk{Nk} d{d} {dt} c{int(causal)} w{window} s{splits} cfg{cfg}",
+              o, lse, ro, rl, dt)
