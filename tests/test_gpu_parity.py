@@ -236,3 +236,23 @@ def test_autotune(fa, d, dt):
         torch.cuda.synchronize()
         check("tuned wrapper", o2.cpu(), l2.cpu(), ro, rl, dt)
     assert any(key[1:6] == (B, H, H, N, d) for key in fa_mod.tuned_configs())
+
+
+def test_plain_random_shapes(fa):
+    """Seeded random shapes, masks and tile configurations of the plain forward."""
+    rng = np.random.default_rng(99)
+    for n in range(16):
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f16", "bf16"]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        N = int(rng.integers(1, 1500))
+        causal = bool(rng.integers(0, 3) > 0)
+        window = int(rng.choice([0, 0, 1, 33, 700])) if causal else 0
+        cfgs = [c for c in range(fa.attn_fwd_num_configs()) if not (d == 128 and c in (4, 5))]
+        cfg = int(rng.choice([-1] + cfgs))
+        q, k, v = inputs(B, G * Hkv, Hkv, N, d, dt, seed=300 + n)
+        ro, rl = oracle_full(q, k, v, causal=causal, window=window)
+        o, lse = run_gpu(q, k, v, causal=causal, window=window, config_id=cfg)
+        check(f"#{n} B{B} Hq{G * Hkv}/{Hkv} N{N} d{d} {dt} c{int(causal)} w{window} cfg{cfg}", o, lse, ro, rl, dt)
