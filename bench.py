@@ -270,7 +270,7 @@ def main() -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+        print("bench.py: this benchmark runs on one GPU only; --gpus must be 1 "
               "(the path shards by (batch, K/V head) with no exchange between GPUs)", file=sys.stderr)
         return 2
 
