@@ -106,6 +106,20 @@ def make_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "f16",
     return q.to(tdt).contiguous(), k.to(tdt).contiguous(), v.to(tdt).contiguous()
 
 
+def make_dout(B: int, Hq: int, N: int, d: int, dtype: str = "f16", seed: int = 0,
+              amplitude: float = 1.0) -> torch.Tensor:
+    """Seeded upstream gradient dO (B,Hq,N,d) for the backward pass: iid
+    N(0,1) times amplitude, rounded to the 16-bit dtype, drawn from its own
+    generator (seed + 104729) so that it does not disturb the Q, K, V
+    stream of the same seed."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 104729)
+    do = torch.randn(B, Hq, N, d, generator=g, dtype=torch.float32)
+    if amplitude != 1.0:
+        do = do * amplitude
+    return do.to(TORCH_DTYPES[dtype]).contiguous()
+
+
 def make_paged_cache(k: torch.Tensor, v: torch.Tensor, page_size: int, seq_lens, seed: int = 0,
                      spare_pages: int = 3):
     """Scatter contiguous host K/V (B, Hkv, Nmax, d) into page pools

@@ -9,7 +9,10 @@ the two meet only in the seeded input generators of ``attn_inputs``.
 mask, row softmax, weighted V sum, log-sum-exp), following "Lab 02 - Forward de
 flash attention en Triton", section "Bloque C", and the standard branch of the
 demo in "Optimizaciones de Atencion", section "FlashAttention: Nunca
-materializar la matriz de atencion".  ``pyref`` holds pure-Python versions for
+materializar la matriz de atencion".  Its backward entry points are the
+gradients of sum(dO * O) for that forward, written out by the chain rule
+(the pages leave the backward out of scope and only say that it recomputes
+the scores and uses the stored log-sum-exp).  ``pyref`` holds pure-Python versions for
 tiny inputs: the same definition with exactly rounded sums, and the tiled
 online-softmax recurrence of that demo, used to pin the C oracle.
 
@@ -63,6 +66,15 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_oracle_fwd_paged.restype = ctypes.c_int
     lib.attn_oracle_fwd_paged.argtypes = [vp, vp, vp, vp, vp, dp, dp, i64, i64, i64, i64, i64, i64, i64, i64,
                                           ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_bwd.restype = ctypes.c_int
+    lib.attn_oracle_bwd.argtypes = [vp, vp, vp, vp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                    ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_bwd_rows.restype = ctypes.c_int
+    lib.attn_oracle_bwd_rows.argtypes = [vp, vp, vp, vp, vp, i64, dp, i64, i64, i64, i64, i64,
+                                         ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
+    lib.attn_oracle_bwd_keys.restype = ctypes.c_int
+    lib.attn_oracle_bwd_keys.argtypes = [vp, vp, vp, vp, dp, dp, vp, i64, dp, dp, i64, i64, i64, i64, i64,
+                                         ctypes.c_int, i64, ctypes.c_float, ctypes.c_int]
     lib.attn_oracle_decode.restype = ctypes.c_double
     lib.attn_oracle_decode.argtypes = [ctypes.c_uint16, ctypes.c_int]
     lib.attn_oracle_max_threads.restype = ctypes.c_int
@@ -162,6 +174,78 @@ def oracle_paged(q, k_pool, v_pool, block_table, seq_lens, *, scale: float, caus
     if rc != 0:
         raise RuntimeError(f"attn_oracle_fwd_paged failed with code {rc}")
     return o, lse
+
+
+def oracle_bwd(q, k, v, dout, *, scale: float, causal: bool = False, window: int = 0,
+               dtype: str = "f16", lib: ctypes.CDLL | None = None):
+    """Whole backward in fp64: the gradients (dq, dk, dv) of sum(dout * O)
+    for the forward O of ``oracle_fwd`` (Nq = Nk).  q and dout (B,Hq,N,d), k
+    and v (B,Hkv,N,d), as uint16 bit patterns or float64.  dk and dv sum the
+    contributions of every query head that shares a K/V head."""
+    lib = lib or load_library()
+    q, k, v, dout = (_as_input(x, dtype) for x in (q, k, v, dout))
+    B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
+    if Nq != Nk or dout.shape != q.shape:
+        raise ValueError("backward oracle: needs Nq == Nk and dout shaped like q")
+    dq = np.zeros(q.shape, np.float64)
+    dk = np.zeros(k.shape, np.float64)
+    dv = np.zeros(k.shape, np.float64)
+    rc = lib.attn_oracle_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                             dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, B, Hq, Hkv, Nq, d,
+                             int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_bwd failed with code {rc}")
+    return dq, dk, dv
+
+
+def oracle_bwd_rows(q, k, v, dout, row_ids, *, scale: float, causal: bool = False, window: int = 0,
+                    dtype: str = "f16", lib: ctypes.CDLL | None = None):
+    """dq of selected query rows (flat (b*Hq + h)*N + i), float64 (n, d)."""
+    lib = lib or load_library()
+    q, k, v, dout = (_as_input(x, dtype) for x in (q, k, v, dout))
+    B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
+    if Nq != Nk or dout.shape != q.shape:
+        raise ValueError("backward oracle: needs Nq == Nk and dout shaped like q")
+    ids = np.ascontiguousarray(np.asarray(row_ids, dtype=np.int64))
+    dq = np.zeros((ids.shape[0], d), np.float64)
+    rc = lib.attn_oracle_bwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                  ids.ctypes.data, ids.shape[0], dq.ctypes.data, B, Hq, Hkv, Nq, d,
+                                  int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_bwd_rows failed with code {rc}")
+    return dq
+
+
+def oracle_bwd_keys(q, k, v, dout, key_ids, *, scale: float, causal: bool = False, window: int = 0,
+                    dtype: str = "f16", lib: ctypes.CDLL | None = None):
+    """dk and dv of selected keys (flat (b*Hkv + hk)*N + j), float64 (n, d)
+    each.  Runs the oracle's own forward first for every row's log-sum-exp
+    and output, from which the Jacobian term D = sum(dout * O) per row."""
+    lib = lib or load_library()
+    q, k, v, dout = (_as_input(x, dtype) for x in (q, k, v, dout))
+    B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
+    if Nq != Nk or dout.shape != q.shape:
+        raise ValueError("backward oracle: needs Nq == Nk and dout shaped like q")
+    o, lse = oracle_fwd(q, k, v, scale=scale, causal=causal, window=window, dtype=dtype, lib=lib)
+    dof = dout.astype(np.float64) if dtype == "f64" else _decode_array(dout, dtype, lib)
+    drow = np.ascontiguousarray((dof * o).sum(-1))
+    lse = np.ascontiguousarray(lse)
+    ids = np.ascontiguousarray(np.asarray(key_ids, dtype=np.int64))
+    dk = np.zeros((ids.shape[0], d), np.float64)
+    dv = np.zeros((ids.shape[0], d), np.float64)
+    rc = lib.attn_oracle_bwd_keys(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                  lse.ctypes.data, drow.ctypes.data, ids.ctypes.data, ids.shape[0],
+                                  dk.ctypes.data, dv.ctypes.data, B, Hq, Hkv, Nq, d,
+                                  int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_bwd_keys failed with code {rc}")
+    return dk, dv
+
+
+def _decode_array(bits: np.ndarray, dtype: str, lib: ctypes.CDLL) -> np.ndarray:
+    """Every distinct bit pattern decoded once by the oracle's own decoder."""
+    table = np.array([lib.attn_oracle_decode(b, DTYPES[dtype]) for b in range(65536)], np.float64)
+    return table[bits]
 
 
 def decode(bits: int, dtype: str, lib: ctypes.CDLL | None = None) -> float:

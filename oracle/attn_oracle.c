@@ -357,3 +357,221 @@ int attn_oracle_fwd_paged(const void *q, const void *k_pool, const void *v_pool,
     }
     return 0;
 }
+
+/*
+ * Backward pass: the gradients of the scalar sum_{b,h,i,c} dO[b,h,i,c] *
+ * O[b,h,i,c] with respect to q, k and v, where O is the forward above (Nq = Nk
+ * = N).  The pages leave the backward out of their scope; they say only that
+ * it recomputes the scores from Q and K instead of storing them, and that the
+ * per-row log-sum-exp is kept for it ("Optimizaciones de Atencion", section
+ * "FlashAttention: Nunca materializar la matriz de atencion"; "Fase 27", the
+ * out-of-scope list).  What it computes is plain calculus on the definition,
+ * written out per query row i of head (b, h) with kv head hk = floor(h / G):
+ *
+ *   P_j   = exp(s_j - m) / l              (the forward's softmax weights)
+ *   dP_j  = sum_c dO[i,c] * v[hk,j,c]     (gradient of the weights)
+ *   D     = sum_j P_j * dP_j              (softmax Jacobian term)
+ *   dS_j  = P_j * (dP_j - D)              (gradient of the scaled scores)
+ *   dq[i,c]    = scale * sum_j dS_j * k[hk,j,c]
+ *   dk[hk,j,c] += scale * dS_j * q[i,c]   (summed over i and the G heads)
+ *   dv[hk,j,c] += P_j * dO[i,c]           (summed over i and the G heads)
+ *
+ * Masked keys have P_j = 0 and so contribute nothing; a row with no visible
+ * key contributes nothing at all.
+ */
+static void bwd_row(const void *q, const void *k, const void *v, const void *dout,
+                    int64_t b, int64_t h, int64_t i, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    int causal, int64_t window, double scale, int dtype,
+                    double *dq_row, double *dk_head, double *dv_head,
+                    double *s, double *qrow, double *dorow)
+{
+    int64_t group = Hq / Hkv;
+    int64_t hk = h / group;
+    int64_t qbase = ((b * Hq + h) * N + i) * d;
+    int64_t kvhead = (b * Hkv + hk) * N * d;
+    int64_t lo, hi;
+    visible_range(i, N, N, causal, window, &lo, &hi);
+    for (int64_t c = 0; c < d; ++c) {
+        dq_row[c] = 0.0;
+        qrow[c] = load_elem(q, dtype, qbase + c);
+        dorow[c] = load_elem(dout, dtype, qbase + c);
+    }
+    if (lo > hi)
+        return;
+    double m = -INFINITY;
+    for (int64_t j = lo; j <= hi; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += qrow[c] * load_elem(k, dtype, kvhead + j * d + c);
+        s[j - lo] = scale * dot;
+        if (s[j - lo] > m)
+            m = s[j - lo];
+    }
+    double l = 0.0;
+    for (int64_t j = lo; j <= hi; ++j)
+        l += exp(s[j - lo] - m);
+    /* s[] now becomes P_j, and dP_j goes into the second half of the buffer */
+    double *dp = s + (hi - lo + 1);
+    double dsum = 0.0;
+    for (int64_t j = lo; j <= hi; ++j) {
+        double p = exp(s[j - lo] - m) / l;
+        double g = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            g += dorow[c] * load_elem(v, dtype, kvhead + j * d + c);
+        s[j - lo] = p;
+        dp[j - lo] = g;
+        dsum += p * g;
+    }
+    for (int64_t j = lo; j <= hi; ++j) {
+        double p = s[j - lo];
+        double ds = p * (dp[j - lo] - dsum);
+        for (int64_t c = 0; c < d; ++c)
+            dq_row[c] += scale * ds * load_elem(k, dtype, kvhead + j * d + c);
+        if (dk_head)
+            for (int64_t c = 0; c < d; ++c) {
+                dk_head[j * d + c] += scale * ds * qrow[c];
+                dv_head[j * d + c] += p * dorow[c];
+            }
+    }
+}
+
+/*
+ * Whole backward.  q, dout, dq: (B, Hq, N, d); k, v, dk, dv: (B, Hkv, N, d);
+ * dq, dk, dv are float64.  One OpenMP task per (batch, kv head), which owns
+ * that head's dk and dv, so nothing is summed across threads.  Returns 0, -1
+ * on bad arguments, -2 when scratch cannot be allocated.
+ */
+int attn_oracle_bwd(const void *q, const void *k, const void *v, const void *dout,
+                    double *dq, double *dk, double *dv,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    int causal, int64_t window, float scale, int dtype)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || N < 0 || d < 1 || Hq % Hkv != 0 || window < 0 ||
+        dtype < ORACLE_F16 || dtype > ORACLE_F64)
+        return -1;
+    int64_t group = Hq / Hkv;
+    int failed = 0;
+    memset(dk, 0, sizeof(double) * (size_t)(B * Hkv * N * d));
+    memset(dv, 0, sizeof(double) * (size_t)(B * Hkv * N * d));
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(2 * (N > 0 ? N : 1)));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *dorow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qrow || !dorow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t g = 0; g < B * Hkv; ++g) {
+                int64_t b = g / Hkv, hk = g % Hkv;
+                double *dkh = dk + g * N * d, *dvh = dv + g * N * d;
+                for (int64_t h = hk * group; h < (hk + 1) * group; ++h)
+                    for (int64_t i = 0; i < N; ++i)
+                        bwd_row(q, k, v, dout, b, h, i, Hq, Hkv, N, d, causal, window, (double)scale,
+                                dtype, dq + ((b * Hq + h) * N + i) * d, dkh, dvh, s, qrow, dorow);
+            }
+        }
+        free(s);
+        free(qrow);
+        free(dorow);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * dq for selected rows only (row_ids[r] = (b * Hq + h) * N + i); each row's
+ * dq needs nothing but that row, so this is the per-row part of the backward
+ * above.  dq: (nrows, d) float64.
+ */
+int attn_oracle_bwd_rows(const void *q, const void *k, const void *v, const void *dout,
+                         const int64_t *row_ids, int64_t nrows, double *dq,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                         int causal, int64_t window, float scale, int dtype)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv != 0 || window < 0 ||
+        dtype < ORACLE_F16 || dtype > ORACLE_F64 || nrows < 0)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_ids[r] < 0 || row_ids[r] >= B * Hq * N)
+            return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(2 * N));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *dorow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qrow || !dorow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t id = row_ids[r];
+                int64_t i = id % N, h = (id / N) % Hq, b = id / (N * Hq);
+                bwd_row(q, k, v, dout, b, h, i, Hq, Hkv, N, d, causal, window, (double)scale, dtype,
+                        dq + r * d, NULL, NULL, s, qrow, dorow);
+            }
+        }
+        free(s);
+        free(qrow);
+        free(dorow);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * dk and dv for selected keys only (key_ids[r] = (b * Hkv + hk) * N + j), for
+ * full-size checks.  A key's gradients need the softmax normaliser and the
+ * Jacobian term D of every row that sees it, so the caller passes them per
+ * query row, as computed by this oracle: lse (B, Hq, N) = m + ln l from the
+ * forward, and drow (B, Hq, N) = sum_j P_j dP_j, which equals sum_c dO[c] *
+ * O[c] for the forward's O.  Then for every head h of the group and every
+ * row i that sees key j:  P = exp(s_ij - lse_i), dP = dO_i . v_j, and
+ *   dk[j] += scale * P * (dP - drow_i) * q_i,   dv[j] += P * dO_i.
+ * dk, dv: (nkeys, d) float64.
+ */
+int attn_oracle_bwd_keys(const void *q, const void *k, const void *v, const void *dout,
+                         const double *lse, const double *drow,
+                         const int64_t *key_ids, int64_t nkeys, double *dk, double *dv,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                         int causal, int64_t window, float scale, int dtype)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv != 0 || window < 0 ||
+        dtype < ORACLE_F16 || dtype > ORACLE_F64 || nkeys < 0)
+        return -1;
+    for (int64_t r = 0; r < nkeys; ++r)
+        if (key_ids[r] < 0 || key_ids[r] >= B * Hkv * N)
+            return -1;
+    int64_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nkeys; ++r) {
+        int64_t id = key_ids[r];
+        int64_t j = id % N, hk = (id / N) % Hkv, b = id / (N * Hkv);
+        int64_t kvhead = (b * Hkv + hk) * N * d;
+        double *dkr = dk + r * d, *dvr = dv + r * d;
+        for (int64_t c = 0; c < d; ++c)
+            dkr[c] = dvr[c] = 0.0;
+        for (int64_t h = hk * group; h < (hk + 1) * group; ++h)
+            for (int64_t i = 0; i < N; ++i) {
+                int64_t lo, hi;
+                visible_range(i, N, N, causal, window, &lo, &hi);
+                if (j < lo || j > hi)
+                    continue;
+                int64_t row = (b * Hq + h) * N + i;
+                double dot = 0.0, g = 0.0;
+                for (int64_t c = 0; c < d; ++c) {
+                    double kc = load_elem(k, dtype, kvhead + j * d + c);
+                    dot += load_elem(q, dtype, row * d + c) * kc;
+                    g += load_elem(dout, dtype, row * d + c) * load_elem(v, dtype, kvhead + j * d + c);
+                }
+                double p = exp((double)scale * dot - lse[row]);
+                double ds = p * (g - drow[row]);
+                for (int64_t c = 0; c < d; ++c) {
+                    dkr[c] += (double)scale * ds * load_elem(q, dtype, row * d + c);
+                    dvr[c] += p * load_elem(dout, dtype, row * d + c);
+                }
+            }
+    }
+    return 0;
+}

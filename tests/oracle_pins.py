@@ -24,7 +24,7 @@ import torch
 
 import oracle
 from oracle import pyref
-from attn_inputs import make_qkv, sine_matrix, to_bits
+from attn_inputs import make_dout, make_qkv, sine_matrix, to_bits
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -488,6 +488,150 @@ def make_paged_cache_f64(k, v, ps, lens, seed):
     return kp.numpy(), vp.numpy(), bt.numpy(), sl.numpy()
 
 
+# ---------------------------------------------------------------------------
+# Backward: the gradients of sum(dO * O).  The pages leave the backward out of
+# scope and print no formula for it, so every pin below is mathematics: finite
+# differences of the (already pinned) forward, the chain rule run by torch
+# autograd over the pages' naive recipe, a hand-derived closed form, and
+# identities of the softmax Jacobian.
+
+def run_bwd(lib, q, k, v, do, scale, causal=False, window=0, dtype="f64"):
+    return oracle.oracle_bwd(q, k, v, do, scale=scale, causal=causal, window=window, dtype=dtype, lib=lib)
+
+
+def _seeded_f64(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def pin_bwd_finite_differences(lib):
+    """Central differences of L = sum(dO * O) through the forward oracle, one
+    input element at a time, equal the backward oracle's gradients (error
+    O(h^2) plus rounding, far below the tolerance)."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 5, 3
+    q, k, v, do = (f64(_seeded_f64(s, 100 + i)) for i, s in enumerate(
+        [(B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d), (B, Hq, N, d)]))
+    scale, h = 0.7, 1e-5
+    for causal, window in MASKS:
+        dq, dk, dv = run_bwd(lib, q, k, v, do, scale, causal, window)
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = dict(args_p)
+                args_p[name], args_m[name] = xp, xm
+                op, _ = run(lib, args_p["q"], args_p["k"], args_p["v"], scale, causal, window)
+                om, _ = run(lib, args_m["q"], args_m["k"], args_m["v"], scale, causal, window)
+                fd[idx] = ((op - om) * do).sum() / (2 * h)
+            close(g, fd, 1e-7, f"finite differences d{name}, causal={causal} W={window}")
+
+
+def pin_bwd_torch_autograd(lib):
+    """The pages' naive recipe ("Lab 02", "Bloque C": Q K^T * scale, -inf
+    mask, softmax, @ V) in torch float64 on the CPU, differentiated by
+    autograd; K/V heads are repeated contiguously for GQA, so autograd sums
+    dk and dv over each group.  Same bit patterns, both dtypes."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 19, 8
+    for dtype in ("f16", "bf16"):
+        q, k, v = (to_bits(t) for t in make_qkv(B, Hq, Hkv, N, d, dtype, seed=21))
+        do = to_bits(make_dout(B, Hq, N, d, dtype, seed=22))
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+        for causal, window in MASKS:
+            tq, tk, tv = (torch.from_numpy(lib_decode(x, dtype)).requires_grad_() for x in (q, k, v))
+            tdo = torch.from_numpy(lib_decode(do, dtype))
+            kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+            vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+            s = (tq @ kk.transpose(-1, -2)) * scale
+            i = torch.arange(N)[:, None]
+            j = torch.arange(N)[None, :]
+            hide = torch.zeros(N, N, dtype=torch.bool)
+            if causal:
+                hide |= j > i
+            if window:
+                hide |= (i - j) >= window
+            o = torch.softmax(s.masked_fill(hide, float("-inf")), dim=-1) @ vv
+            (o * tdo).sum().backward()
+            dq, dk, dv = run_bwd(lib, q, k, v, do, scale, causal, window, dtype)
+            what = f"{dtype} causal={causal} W={window}"
+            close(dq, tq.grad.numpy(), 1e-12, f"autograd dq {what}")
+            close(dk, tk.grad.numpy(), 1e-12, f"autograd dk {what}")
+            close(dv, tv.grad.numpy(), 1e-12, f"autograd dv {what}")
+
+
+def pin_bwd_two_key_closed_form(lib):
+    """Hand-derived, d=1: q = (1, 0), k = (ln 3 / scale, 0), v = (4, 8),
+    dO = (1, 2).  Row 0 weighs the keys 3:1: dP = (4, 8), D = 5,
+    dS = (-3/4, 3/4), so dq_0 = -(3/4) ln 3, dk += scale * (-3/4, 3/4),
+    dv += (3/4, 1/4).  Row 1 (q = 0) weighs them 1:1: dP = (8, 16), D = 12,
+    dS = (-2, 2), dq_1 = -2 ln 3, dk += 0, dv += (1, 1).  Causal: row 0 sees
+    key 0 alone, so dS = 0 and dv += (1, 0); row 1 is unchanged."""
+    for scale in (1.0, 0.5, 0.25):
+        q = f64([[[[1.0], [0.0]]]])
+        k = f64([[[[math.log(3.0) / scale], [0.0]]]])
+        v = f64([[[[4.0], [8.0]]]])
+        do = f64([[[[1.0], [2.0]]]])
+        dq, dk, dv = run_bwd(lib, q, k, v, do, scale)
+        l3 = math.log(3.0)
+        close(dq[0, 0, :, 0], [-0.75 * l3, -2.0 * l3], 1e-14, f"two-key dq, scale {scale}")
+        close(dk[0, 0, :, 0], [-0.75 * scale, 0.75 * scale], 1e-14, f"two-key dk, scale {scale}")
+        close(dv[0, 0, :, 0], [1.75, 1.25], 1e-14, f"two-key dv, scale {scale}")
+        dq, dk, dv = run_bwd(lib, q, k, v, do, scale, causal=True)
+        close(dq[0, 0, :, 0], [0.0, -2.0 * l3], 1e-14, f"two-key causal dq, scale {scale}")
+        close(dk[0, 0, :, 0], [0.0, 0.0], 1e-14, f"two-key causal dk, scale {scale}")
+        close(dv[0, 0, :, 0], [2.0, 1.0], 1e-14, f"two-key causal dv, scale {scale}")
+
+
+def pin_bwd_identities(lib):
+    """Identities of the softmax Jacobian, on GQA shapes under every mask:
+    - rows of dS sum to 0, so sum_j dk_j = 0 for every (batch, K/V head);
+    - rows of P sum to 1, so sum_j dv_j = sum over the group's rows of dO;
+    - V rows all equal make dP constant along a row, so dq = dk = 0;
+    - under W = 1 each row sees only itself: dq = dk = 0 and dv_j is the sum
+      of dO row j over the group's heads."""
+    B, Hq, Hkv, N, d = 2, 6, 2, 23, 8
+    G = Hq // Hkv
+    for dtype in ("f16", "bf16"):
+        q, k, v = (to_bits(t) for t in make_qkv(B, Hq, Hkv, N, d, dtype, seed=31))
+        do = to_bits(make_dout(B, Hq, N, d, dtype, seed=32))
+        dod = lib_decode(do, dtype)
+        group_do = dod.reshape(B, Hkv, G, N, d).sum(axis=2)
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+        for causal, window in MASKS:
+            what = f"{dtype} causal={causal} W={window}"
+            dq, dk, dv = run_bwd(lib, q, k, v, do, scale, causal, window, dtype)
+            close(dk.sum(axis=2), np.zeros((B, Hkv, d)), 1e-12, f"sum_j dk_j {what}")
+            close(dv.sum(axis=2), group_do.sum(axis=2), 1e-11, f"sum_j dv_j {what}")
+            vconst = np.ascontiguousarray(np.broadcast_to(v[:, :, :1, :], v.shape))
+            dq, dk, dv = run_bwd(lib, q, k, vconst, do, scale, causal, window, dtype)
+            close(dq, np.zeros_like(dq), 1e-12, f"constant V: dq {what}")
+            close(dk, np.zeros_like(dk), 1e-12, f"constant V: dk {what}")
+        dq, dk, dv = run_bwd(lib, q, k, v, do, scale, True, 1, dtype)
+        close(dq, np.zeros_like(dq), 0.0, f"W=1 dq {dtype}")
+        close(dk, np.zeros_like(dk), 0.0, f"W=1 dk {dtype}")
+        close(dv, group_do, 1e-13, f"W=1 dv {dtype}")
+
+
+def pin_bwd_sampled_entries(lib):
+    """The per-row dq and per-key dk/dv entry points (used at full sizes)
+    agree with the whole backward."""
+    B, Hq, Hkv, N, d = 2, 4, 1, 29, 16
+    q, k, v = (to_bits(t) for t in make_qkv(B, Hq, Hkv, N, d, "bf16", seed=41))
+    do = to_bits(make_dout(B, Hq, N, d, "bf16", seed=42))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    rows = np.array([0, 5, N - 1, N + 3, 3 * N + 7, B * Hq * N - 1])
+    keys = np.array([0, 1, N - 1, N + 2, B * Hkv * N - 1])
+    for causal, window in MASKS:
+        kw = dict(scale=scale, causal=causal, window=window, dtype="bf16", lib=lib)
+        dq, dk, dv = oracle.oracle_bwd(q, k, v, do, **kw)
+        what = f"causal={causal} W={window}"
+        close(oracle.oracle_bwd_rows(q, k, v, do, rows, **kw), dq.reshape(-1, d)[rows], 1e-13, f"rows dq {what}")
+        sk, sv = oracle.oracle_bwd_keys(q, k, v, do, keys, **kw)
+        close(sk, dk.reshape(-1, d)[keys], 1e-12, f"keys dk {what}")
+        close(sv, dv.reshape(-1, d)[keys], 1e-12, f"keys dv {what}")
+
+
 ALL_PINS = [
     pin_decoders,
     pin_tiled_demo,
@@ -509,4 +653,9 @@ ALL_PINS = [
     pin_split_kv_merge,
     pin_paged_matches_contiguous,
     pin_paged_gather_order,
+    pin_bwd_finite_differences,
+    pin_bwd_torch_autograd,
+    pin_bwd_two_key_closed_form,
+    pin_bwd_identities,
+    pin_bwd_sampled_entries,
 ]

@@ -48,6 +48,21 @@ MUTANTS = {
     "bf16_bias_off": ("mag = ldexp((double)(frac | 0x80), expo - 134);",
                       "mag = ldexp((double)(frac | 0x80), expo - 133);"),
     "f16_subnormal_off": ("mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
+    "bwd_jacobian_term_dropped": ("double ds = p * (dp[j - lo] - dsum);", "double ds = p * dp[j - lo];"),
+    "bwd_jacobian_sign_flipped": ("double ds = p * (dp[j - lo] - dsum);", "double ds = p * (dsum - dp[j - lo]);"),
+    "bwd_dq_scale_dropped": ("dq_row[c] += scale * ds * load_elem(k, dtype, kvhead + j * d + c);",
+                             "dq_row[c] += ds * load_elem(k, dtype, kvhead + j * d + c);"),
+    "bwd_dq_uses_v": ("dq_row[c] += scale * ds * load_elem(k, dtype, kvhead + j * d + c);",
+                      "dq_row[c] += scale * ds * load_elem(v, dtype, kvhead + j * d + c);"),
+    "bwd_dk_uses_dout": ("dk_head[j * d + c] += scale * ds * qrow[c];", "dk_head[j * d + c] += scale * ds * dorow[c];"),
+    "bwd_dv_uses_ds": ("dv_head[j * d + c] += p * dorow[c];", "dv_head[j * d + c] += ds * dorow[c];"),
+    "bwd_dp_uses_k": ("g += dorow[c] * load_elem(v, dtype, kvhead + j * d + c);",
+                      "g += dorow[c] * load_elem(k, dtype, kvhead + j * d + c);"),
+    "bwd_unnormalised_p": ("double p = exp(s[j - lo] - m) / l;", "double p = exp(s[j - lo] - m);"),
+    "bwd_gqa_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h)\n                    for (int64_t i = 0; i < N; ++i)\n                        bwd_row",
+                                "for (int64_t h = hk * group; h < hk * group + 1; ++h)\n                    for (int64_t i = 0; i < N; ++i)\n                        bwd_row"),
+    "bwd_keys_scale_dropped": ("double p = exp((double)scale * dot - lse[row]);", "double p = exp(dot - lse[row]);"),
+    "bwd_keys_jacobian_dropped": ("double ds = p * (g - drow[row]);", "double ds = p * g;"),
     "max_not_tracked": ("if (s[j - lo] > m)\n            m = s[j - lo];", "if (j == lo)\n            m = s[j - lo];"),
 }
 
