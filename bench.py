@@ -94,10 +94,16 @@ def algorithmic_bytes(w) -> float:
             + 4.0 * w.B * w.Hq * w.N)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str = "fwd") -> str:
+    """Hash of the sources the forward kernels (family "fwd") or the backward
+    kernels ("bwd") are built from: the files of csrc/ with the family's
+    prefix plus the shared helpers."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "flashattention_forward_05_amd", "csrc")
+    other = "attn_bwd" if family == "fwd" else "attn_fwd"
     for fn in sorted(os.listdir(csrc)):
+        if fn.startswith(other) and fn != "attn_fwd_common.hpp":
+            continue
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]

@@ -23,12 +23,20 @@ Paged K/V ("00 - Por que la atencion domina la inferencia", section
 "PagedAttention es un problema distinto"): ``attn_fwd_paged``,
 ``attn_fwd_paged_ex``, ``attn_fwd_paged_validate``, ``attn_fwd_paged_plan``,
 ``attn_fwd_paged_workspace_size`` and ``flash_attn_forward_paged``.
+
+Backward (``include/attn_bwd.h``): ``attn_bwd``, ``attn_bwd_validate``,
+``attn_bwd_workspace_size`` and ``flash_attn_backward(q, k, v, o, lse, dout)``,
+the gradients of sum(dout * o) computed from the forward's log-sum-exp with
+the scores recomputed tile by tile.
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
     ATTN_F16,
     STATUS,
     AttnError,
+    attn_bwd,
+    attn_bwd_validate,
+    attn_bwd_workspace_size,
     attn_fwd,
     attn_fwd_autotune,
     attn_fwd_config_desc,
@@ -48,6 +56,7 @@ from ._binding import (  # noqa: F401
     attn_fwd_splitkv_workspace_size,
     attn_fwd_validate,
     attn_status_str,
+    flash_attn_backward,
     flash_attn_forward,
     flash_attn_forward_paged,
     flash_attn_forward_splitkv,

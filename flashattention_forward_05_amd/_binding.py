@@ -84,6 +84,13 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_paged_plan.restype = cint
     lib.attn_fwd_paged_workspace_size.argtypes = geo
     lib.attn_fwd_paged_workspace_size.restype = i64
+    bwd = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cint, i64, f32, cint, vp, i64]
+    lib.attn_bwd.argtypes = bwd + [vp]
+    lib.attn_bwd.restype = cint
+    lib.attn_bwd_validate.argtypes = bwd
+    lib.attn_bwd_validate.restype = cint
+    lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.attn_bwd_workspace_size.restype = i64
     _lib = lib
     return lib
 
@@ -437,3 +444,68 @@ def flash_attn_forward_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_l
                           num_pages, max_pages, max_seq_len, causal, window, scale, dtype, num_splits, config_id,
                           workspace, ws_bytes, torch.cuda.current_stream(q.device).cuda_stream)
     return out, lse
+
+
+# ---- backward pass (include/attn_bwd.h): gradients of sum(dO * O) from the
+# forward's o and lse, scores recomputed tile by tile
+
+def attn_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
+    """Bytes of workspace attn_bwd needs (-1 for a shape it would reject)."""
+    return int(load_library().attn_bwd_workspace_size(B, Hq, Hkv, N, d))
+
+
+def attn_bwd_validate(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale, dtype,
+                      workspace=None, workspace_bytes=0) -> int:
+    """Host-side argument checks only; returns the status code."""
+    return load_library().attn_bwd_validate(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), window, scale,
+                                            dtype, _ptr(workspace), int(workspace_bytes))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale, dtype,
+             workspace, workspace_bytes, stream=None) -> None:
+    """Enqueue the backward on `stream` (default: torch's current stream)."""
+    rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, Hq, Hkv, N, d, int(causal), window, scale, dtype, _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_bwd")
+
+
+def flash_attn_backward(q, k, v, o, lse, dout, causal: bool = True, window: int = 0, scale: float | None = None,
+                        workspace=None):
+    """Gradients (dq, dk, dv) of sum(dout * o) for o, lse = flash_attn_forward(q,
+    k, v, causal, window, scale).  Same shapes and dtype rules as the forward;
+    dout is shaped like q.  The workspace is allocated with torch when not
+    given."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype not in (torch.float16, torch.bfloat16) or t.dtype != q.dtype:
+            raise TypeError(f"{name} must be float16 or bfloat16 like q, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (B, H, N, d), got shape {tuple(t.shape)}")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32:
+        raise TypeError("lse must be the forward's float32 log-sum-exp tensor")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)} disagree")
+    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("o and dout must be shaped like q, lse (B, Hq, N)")
+    Hkv = k.shape[1]
+    q, k, v, o, dout, lse = (t.contiguous() for t in (q, k, v, o, dout, lse))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dtype = ATTN_F16 if q.dtype == torch.float16 else ATTN_BF16
+    need = attn_bwd_workspace_size(B, Hq, Hkv, N, d)
+    if need < 0:
+        raise AttnError(2, "attn_bwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale, dtype, workspace,
+                 workspace.numel() * workspace.element_size(), torch.cuda.current_stream(q.device).cuda_stream)
+    return dq, dk, dv

@@ -17,15 +17,17 @@ SOURCES = [
     (os.path.join(CSRC, "attn_fwd_d128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_paged64.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_paged128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
+    (os.path.join(CSRC, "attn_bwd.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_pipe.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Rpass-analysis=kernel-resource-usage"]),
 ]
 # Kernels whose loads are tracked by explicit vmcnt waits must not touch
 # scratch memory (a spill reload would count as an outstanding load).
-NO_SCRATCH = ("attn_fwd_pipe_kernel", "attn_fwd_kernel", "attn_fwd_pingpong_kernel")
+NO_SCRATCH = ("attn_fwd_pipe_kernel", "attn_fwd_kernel", "attn_fwd_pingpong_kernel", "attn_bwd_dkdv_kernel",
+              "attn_bwd_dq_kernel")
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp", "attn_fwd_pingpong.hpp",
                                             "attn_fwd_pipe.hpp", "attn_fwd_launch.hpp",
                                             "attn_fwd_merge.hpp", "attn_fwd_lockstep.hpp")] + [
-    os.path.join(INCLUDE, "attn_fwd.h")]
+    os.path.join(INCLUDE, "attn_fwd.h"), os.path.join(INCLUDE, "attn_bwd.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

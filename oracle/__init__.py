@@ -219,33 +219,48 @@ def oracle_bwd_rows(q, k, v, dout, row_ids, *, scale: float, causal: bool = Fals
 def oracle_bwd_keys(q, k, v, dout, key_ids, *, scale: float, causal: bool = False, window: int = 0,
                     dtype: str = "f16", lib: ctypes.CDLL | None = None):
     """dk and dv of selected keys (flat (b*Hkv + hk)*N + j), float64 (n, d)
-    each.  Runs the oracle's own forward first for every row's log-sum-exp
-    and output, from which the Jacobian term D = sum(dout * O) per row."""
+    each.  For every (batch, K/V head) that holds a selected key, runs the
+    oracle's own forward over that group's query heads first, for each row's
+    log-sum-exp and output, from which the Jacobian term D = sum(dout * O)."""
     lib = lib or load_library()
     q, k, v, dout = (_as_input(x, dtype) for x in (q, k, v, dout))
     B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
     if Nq != Nk or dout.shape != q.shape:
         raise ValueError("backward oracle: needs Nq == Nk and dout shaped like q")
-    o, lse = oracle_fwd(q, k, v, scale=scale, causal=causal, window=window, dtype=dtype, lib=lib)
-    dof = dout.astype(np.float64) if dtype == "f64" else _decode_array(dout, dtype, lib)
-    drow = np.ascontiguousarray((dof * o).sum(-1))
-    lse = np.ascontiguousarray(lse)
-    ids = np.ascontiguousarray(np.asarray(key_ids, dtype=np.int64))
+    N, G = Nq, Hq // Hkv
+    ids = np.asarray(key_ids, dtype=np.int64)
+    if ids.size and (ids.min() < 0 or ids.max() >= B * Hkv * N):
+        raise ValueError("key id out of range")
     dk = np.zeros((ids.shape[0], d), np.float64)
     dv = np.zeros((ids.shape[0], d), np.float64)
-    rc = lib.attn_oracle_bwd_keys(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
-                                  lse.ctypes.data, drow.ctypes.data, ids.ctypes.data, ids.shape[0],
-                                  dk.ctypes.data, dv.ctypes.data, B, Hq, Hkv, Nq, d,
-                                  int(bool(causal)), int(window), float(scale), DTYPES[dtype])
-    if rc != 0:
-        raise RuntimeError(f"attn_oracle_bwd_keys failed with code {rc}")
+    table = None
+    for grp in np.unique(ids // N):
+        b, hk = divmod(int(grp), Hkv)
+        sel = np.nonzero(ids // N == grp)[0]
+        qs = np.ascontiguousarray(q[b:b + 1, hk * G:(hk + 1) * G])
+        dos = np.ascontiguousarray(dout[b:b + 1, hk * G:(hk + 1) * G])
+        ks = np.ascontiguousarray(k[b:b + 1, hk:hk + 1])
+        vs = np.ascontiguousarray(v[b:b + 1, hk:hk + 1])
+        o, lse = oracle_fwd(qs, ks, vs, scale=scale, causal=causal, window=window, dtype=dtype, lib=lib)
+        if dtype == "f64":
+            dof = dos
+        else:
+            if table is None:
+                table = np.array([lib.attn_oracle_decode(x, DTYPES[dtype]) for x in range(65536)], np.float64)
+            dof = table[dos]
+        drow = np.ascontiguousarray((dof * o).sum(-1))
+        lse = np.ascontiguousarray(lse)
+        local = np.ascontiguousarray(ids[sel] % N)
+        gk = np.zeros((sel.shape[0], d), np.float64)
+        gv = np.zeros((sel.shape[0], d), np.float64)
+        rc = lib.attn_oracle_bwd_keys(qs.ctypes.data, ks.ctypes.data, vs.ctypes.data, dos.ctypes.data,
+                                      lse.ctypes.data, drow.ctypes.data, local.ctypes.data, local.shape[0],
+                                      gk.ctypes.data, gv.ctypes.data, 1, G, 1, N, d,
+                                      int(bool(causal)), int(window), float(scale), DTYPES[dtype])
+        if rc != 0:
+            raise RuntimeError(f"attn_oracle_bwd_keys failed with code {rc}")
+        dk[sel], dv[sel] = gk, gv
     return dk, dv
-
-
-def _decode_array(bits: np.ndarray, dtype: str, lib: ctypes.CDLL) -> np.ndarray:
-    """Every distinct bit pattern decoded once by the oracle's own decoder."""
-    table = np.array([lib.attn_oracle_decode(b, DTYPES[dtype]) for b in range(65536)], np.float64)
-    return table[bits]
 
 
 def decode(bits: int, dtype: str, lib: ctypes.CDLL | None = None) -> float:

@@ -385,8 +385,7 @@ static void bwd_row(const void *q, const void *k, const void *v, const void *dou
                     double *dq_row, double *dk_head, double *dv_head,
                     double *s, double *qrow, double *dorow)
 {
-    int64_t group = Hq / Hkv;
-    int64_t hk = h / group;
+    int64_t hk = h / (Hq / Hkv);
     int64_t qbase = ((b * Hq + h) * N + i) * d;
     int64_t kvhead = (b * Hkv + hk) * N * d;
     int64_t lo, hi;
@@ -402,10 +401,9 @@ static void bwd_row(const void *q, const void *k, const void *v, const void *dou
     for (int64_t j = lo; j <= hi; ++j) {
         double dot = 0.0;
         for (int64_t c = 0; c < d; ++c)
-            dot += qrow[c] * load_elem(k, dtype, kvhead + j * d + c);
-        s[j - lo] = scale * dot;
-        if (s[j - lo] > m)
-            m = s[j - lo];
+            dot += load_elem(k, dtype, kvhead + j * d + c) * qrow[c];
+        s[j - lo] = dot * scale;
+        m = s[j - lo] > m ? s[j - lo] : m;
     }
     double l = 0.0;
     for (int64_t j = lo; j <= hi; ++j)

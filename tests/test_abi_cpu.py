@@ -254,3 +254,49 @@ def test_autotune_rejects_before_touching_the_gpu():
     bad = (A, 2 * A, 3 * A, 4 * A, None, 1, 3, 2, 8, 64, 0, 0, 0.1, 0)      # Hq % Hkv != 0
     assert lib.attn_fwd_autotune(*bad, 10, ctypes.byref(best), None, None) == 2
     assert best.value == -7
+
+
+# ---- backward (include/attn_bwd.h)
+BG = dict(q=A, k=2 * A, v=3 * A, o=4 * A, dout=5 * A, lse=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
+          B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, window=0, scale=0.125, dtype=0, ws=10 * A, wsb=1 << 16)
+
+
+def validate_bwd(**over):
+    a = dict(BG, **over)
+    return fa.attn_bwd_validate(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["window"], a["scale"],
+                                a["dtype"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, 0),
+    ({"N": 0, "q": None, "k": None, "v": None, "o": None, "dout": None, "lse": None, "dq": None, "dk": None,
+      "dv": None, "ws": None, "wsb": 0}, 0),
+    ({"q": None}, 1), ({"o": None}, 1), ({"dout": None}, 1), ({"lse": None}, 1), ({"dq": None}, 1),
+    ({"dk": None}, 1), ({"dv": None}, 1), ({"ws": None}, 1),
+    ({"B": 0}, 2), ({"Hq": 3}, 2), ({"N": -1}, 2), ({"N": (1 << 24) + 1}, 2),
+    ({"d": 96}, 3), ({"dtype": 2}, 3), ({"window": 8, "causal": 0}, 3), ({"window": -1}, 3),
+    ({"scale": float("nan")}, 4),
+    ({"q": A + 8}, 5), ({"dk": 8 * A + 4}, 5), ({"ws": 10 * A + 8}, 5), ({"lse": 6 * A + 2}, 5),
+    ({"dq": A}, 6), ({"dk": 5 * A + 16}, 6), ({"dv": 8 * A}, 6), ({"ws": 6 * A}, 6), ({"ws": 9 * A + 32}, 6),
+    ({"wsb": 2 * 4 * 128 * 8 - 1}, 9),
+])
+def test_bwd_validate_codes(over, code):
+    assert validate_bwd(**over) == code
+
+
+def test_bwd_workspace_size():
+    # 8 bytes per query row, rows padded to a multiple of 64 per head
+    assert fa.attn_bwd_workspace_size(2, 4, 2, 100, 64) == 2 * 4 * 128 * 8
+    assert fa.attn_bwd_workspace_size(1, 1, 1, 64, 128) == 64 * 8
+    assert fa.attn_bwd_workspace_size(1, 1, 1, 0, 128) == 0
+    assert fa.attn_bwd_workspace_size(1, 3, 2, 64, 64) == -1
+    assert fa.attn_bwd_workspace_size(1, 1, 1, 64, 96) == -1
+    assert validate_bwd(wsb=2 * 4 * 128 * 8) == 0
+
+
+def test_bwd_rejects_before_touching_the_gpu():
+    with pytest.raises(fa.AttnError) as e:
+        fa.attn_bwd(None, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A, 1, 1, 1, 8, 64, 0, 0, 0.1, 0,
+                    10 * A, 1 << 16, 0)
+    assert e.value.status == 1

@@ -1,0 +1,167 @@
+"""GPU parity of the backward pass (attn_bwd through the C ABI) against the
+fp64 oracle's gradients of sum(dO * O), on the same seeded inputs.
+
+The forward's o and lse come from the HIP forward (as a caller would pass
+them); the oracle differentiates the exact forward.  Tolerance, per output
+tensor X in {dq, dk, dv}: max|X_gpu - X_ref| < 4 u max|X_ref|, with u the
+unit roundoff of the 16-bit type (2^-11 fp16, 2^-8 bf16).  The kernels round
+P and dS to that type as MFMA operands and round the outputs once; a numpy
+emulation of exactly that scheme against the same oracle stays below 1.35 u
+on the lab and GQA shapes, so 4 u leaves a margin of about 3 while any
+error in a term (a wrong mask, scale, head map or transposed operand) shows
+up at the size of the gradient itself.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_inputs import make_dout, make_qkv, to_bits
+from gpu_helpers import DT_CODE, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_BWD = {"f16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    return need_gpu()
+
+
+def run_bwd(q, k, v, do, *, causal, window=0, scale=None, poison=True):
+    """Host tensors in; HIP forward then HIP backward; host (dq, dk, dv) out."""
+    import flashattention_forward_05_amd as fa
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    dt = DT_CODE["f16" if q.dtype == torch.float16 else "bf16"]
+    stream = torch.cuda.current_stream().cuda_stream
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    fa.attn_fwd(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dt, stream)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    need = fa.attn_bwd_workspace_size(B, Hq, Hkv, N, d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if poison:
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        ws.fill_(0xFF)
+    fa.attn_bwd(qd, kd, vd, o, dod, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale, dt, ws, ws.numel(),
+                stream)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check_grads(label, got, ref, dtype):
+    worst = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        gd = g.to(torch.float64).numpy().reshape(r.shape)
+        assert np.isfinite(gd).all(), f"{label}: non-finite {name}"
+        scale = float(np.abs(r).max()) if r.size else 0.0
+        err = float(np.abs(gd - r).max()) if r.size else 0.0
+        rel = err / scale if scale > 0 else err
+        worst.append(rel)
+        assert rel < TOL_BWD[dtype], f"{label}: {name} error {err:.3e} = {rel:.2e} x max|ref| >= {TOL_BWD[dtype]:.2e}"
+    say(f"  {label}: max error / max|ref|: dq {worst[0]:.2e}, dk {worst[1]:.2e}, dv {worst[2]:.2e} "
+        f"(tol {TOL_BWD[dtype]:.2e})")
+    return worst
+
+
+def full_case(B, Hq, Hkv, N, d, dtype, causal, window=0, seed=0, scale=None):
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, dtype, seed=seed)
+    do = make_dout(B, Hq, N, d, dtype, seed=seed)
+    label = f"bwd B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} W={window} seed={seed}"
+    if scale is not None:
+        label += f" scale={scale}"
+    say(f"case {label}")
+    s = 1.0 / math.sqrt(d) if scale is None else scale
+    got = run_bwd(q, k, v, do, causal=causal, window=window, scale=s)
+    ref = oracle.oracle_bwd(to_bits(q), to_bits(k), to_bits(v), to_bits(do), scale=float(np.float32(s)),
+                            causal=causal, window=window, dtype=dtype)
+    return check_grads(label, got, ref, dtype)
+
+
+# ---- the lab shapes (2, 4, N, 64) fp16, causal and not, with a ragged tail
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [64, 256, 1000])
+def test_bwd_lab(fa, N, causal):
+    full_case(2, 4, 4, N, 64, "f16", causal)
+
+
+# ---- GQA / MQA, d = 128, bf16 and fp16, every mask, ragged lengths
+@pytest.mark.parametrize("mask", [(False, 0), (True, 0), (True, 100), (True, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bwd_gqa_d128(fa, dtype, mask):
+    causal, window = mask
+    full_case(1, 8, 2, 333, 128, dtype, causal, window)
+
+
+@pytest.mark.parametrize("mask", [(False, 0), (True, 0), (True, 77)])
+def test_bwd_mqa(fa, mask):
+    causal, window = mask
+    full_case(2, 4, 1, 257, 128, "bf16", causal, window, seed=3)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 63, 65, 130])
+def test_bwd_short_and_ragged(fa, N, d):
+    full_case(1, 2, 1, N, d, "f16", True, seed=N)
+    full_case(1, 2, 2, N, d, "bf16", False, seed=N + 1)
+
+
+def test_bwd_window_d64(fa):
+    full_case(2, 4, 2, 700, 64, "bf16", True, 129, seed=5)
+
+
+def test_bwd_negative_and_odd_scale(fa):
+    full_case(1, 4, 2, 200, 64, "f16", True, scale=-0.1, seed=6)
+    full_case(1, 4, 4, 200, 128, "bf16", False, scale=0.3, seed=7)
+
+
+def test_bwd_deterministic(fa):
+    q, k, v = make_qkv(1, 8, 2, 500, 128, "bf16", seed=9)
+    do = make_dout(1, 8, 500, 128, "bf16", seed=9)
+    say("case bwd determinism (1, 8/2, 500, 128) bf16 causal")
+    a = run_bwd(q, k, v, do, causal=True)
+    b = run_bwd(q, k, v, do, causal=True, poison=False)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+# ---- full size, sampled: dq rows and dk / dv keys the oracle computes one by one
+def sampled_case(B, Hq, Hkv, N, d, dtype, causal, window=0, seed=0, n_rows=48, n_keys=24):
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, dtype, seed=seed)
+    do = make_dout(B, Hq, N, d, dtype, seed=seed)
+    label = f"bwd sampled B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} W={window}"
+    say(f"case {label}")
+    dq, dk, dv = run_bwd(q, k, v, do, causal=causal, window=window)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, N - 1, N // 2], rng.integers(0, B * Hq * N, n_rows)]))
+    # keys of one (batch, K/V head) group: the oracle's forward runs per group
+    grp = int(rng.integers(0, B * Hkv))
+    keys = np.unique(np.concatenate([[0, 1, 63, 64, N - 1], rng.integers(0, N, n_keys)])) + grp * N
+    s = float(np.float32(1.0 / math.sqrt(d)))
+    kw = dict(scale=s, causal=causal, window=window, dtype=dtype)
+    bits = [to_bits(t) for t in (q, k, v, do)]
+    rq = oracle.oracle_bwd_rows(*bits, rows, **kw)
+    rk, rv = oracle.oracle_bwd_keys(*bits, keys, **kw)
+    # the scale of each tensor is taken over the sampled reference entries
+    check_grads(label, (dq.reshape(-1, d)[rows], dk.reshape(-1, d)[keys], dv.reshape(-1, d)[keys]),
+                (rq, rk, rv), dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_lab_n4096_sampled(fa, causal):
+    sampled_case(2, 4, 4, 4096, 64, "f16", causal)
+
+
+def test_bwd_gqa_n8192_sampled(fa):
+    sampled_case(4, 32, 8, 8192, 128, "bf16", True, n_rows=32, n_keys=12)

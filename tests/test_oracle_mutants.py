@@ -61,6 +61,9 @@ MUTANTS = {
     "bwd_unnormalised_p": ("double p = exp(s[j - lo] - m) / l;", "double p = exp(s[j - lo] - m);"),
     "bwd_gqa_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h)\n                    for (int64_t i = 0; i < N; ++i)\n                        bwd_row",
                                 "for (int64_t h = hk * group; h < hk * group + 1; ++h)\n                    for (int64_t i = 0; i < N; ++i)\n                        bwd_row"),
+    "bwd_gqa_modulo_map": ("int64_t hk = h / (Hq / Hkv);", "int64_t hk = h % Hkv;"),
+    "bwd_scores_use_v": ("dot += load_elem(k, dtype, kvhead + j * d + c) * qrow[c];",
+                         "dot += load_elem(v, dtype, kvhead + j * d + c) * qrow[c];"),
     "bwd_keys_scale_dropped": ("double p = exp((double)scale * dot - lse[row]);", "double p = exp(dot - lse[row]);"),
     "bwd_keys_jacobian_dropped": ("double ds = p * (g - drow[row]);", "double ds = p * g;"),
     "max_not_tracked": ("if (s[j - lo] > m)\n            m = s[j - lo];", "if (j == lo)\n            m = s[j - lo];"),
