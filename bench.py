@@ -109,18 +109,67 @@ def kernel_source_hash(family: str = "fwd") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_label: str):
+def traffic_from_profiles(kernel_label: str, family: str = "fwd"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", "traffic.json" if family == "fwd" else "traffic_bwd.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_hash():
+    if rec.get("kernel_source_sha") != kernel_source_hash(family):
         return None
     ent = rec.get("kernels", {}).get(kernel_label)
     return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def backward_bytes(w) -> float:
+    """Bytes the backward must move at least: q, o, dO, k, v and lse read,
+    dq, dk, dv written."""
+    return (3 * 2.0 * w.B * w.Hq * w.N * w.d + 2 * 2.0 * w.B * w.Hkv * w.N * w.d + 4.0 * w.B * w.Hq * w.N
+            + 2.0 * w.B * w.Hq * w.N * w.d + 2 * 2.0 * w.B * w.Hkv * w.N * w.d)
+
+
+def cpu_baseline_backward(workloads, budget_s: float):
+    """The oracle's backward, untuned, on a seeded random sample of query rows
+    of each variant (its per-row entry point: scores, softmax weights, dP, D,
+    dS and the row's dq), in chunks of 64 rows until that variant's share of
+    the time budget is spent.  FLOPs counted per row: 6*d per visible key
+    (three of the five products of the backward)."""
+    import numpy as np
+
+    import oracle
+    from attn_inputs import make_dout, make_workload, to_bits
+
+    oracle.load_library()
+    flops = elapsed = 0.0
+    rows_done = 0
+    per_variant = budget_s / len(workloads)
+    rng = np.random.default_rng(0)
+    for w in workloads:
+        q, k, v = (to_bits(t) for t in make_workload(w, seed=0))
+        do = to_bits(make_dout(w.B, w.Hq, w.N, w.d, w.dtype, seed=0))
+        ids = rng.permutation(w.B * w.Hq * w.N).astype(np.int64)
+        t_var = 0.0
+        for start in range(0, len(ids), 64):
+            chunk = ids[start:start + 64]
+            t0 = time.perf_counter()
+            oracle.oracle_bwd_rows(q, k, v, do, chunk, scale=float(np.float32(w.scale)), causal=w.causal,
+                                   window=w.window, dtype=w.dtype)
+            t_var += time.perf_counter() - t0
+            rows_done += len(chunk)
+            flops += sum(6.0 * w.d * visible_keys(int(r) % w.N, w.N, w.causal, w.window) for r in chunk)
+            if t_var > per_variant:
+                break
+        elapsed += t_var
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle backward (per-row dq entry point) on random query rows of every variant, "
+                   f"about {per_variant:.1f} s each ({rows_done} rows, {flops / 1e9:.2f} GFLOP in {elapsed:.1f} s)"),
+    }
 
 
 def cpu_baseline(workloads, budget_s: float):
@@ -243,6 +292,9 @@ def main() -> int:
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="keep the K/V of decoding workloads in pages of this many tokens (random page order) "
                          "and run the paged entry point")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (attn_bwd) of each variant instead of the forward; "
+                         "FLOPs are 2.5x the forward's (the five products of the backward)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a summary of a rocprofv3 kernel-trace CSV dir")
@@ -332,19 +384,37 @@ def main() -> int:
         flops = workload_flops(w)
         nbytes = algorithmic_bytes(w)
         cfg = args.config
+        bwd = None
+        if args.backward:
+            if split or paged:
+                print("bench.py: --backward needs square (Nq = Nk) workloads", file=sys.stderr)
+                return 2
+            from attn_inputs import make_dout
+            fa.attn_fwd_ex(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, w.scale, dt, cfg,
+                           stream.cuda_stream)
+            need = fa.attn_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d)
+            bwd = dict(do=make_dout(w.B, w.Hq, w.N, w.d, w.dtype, seed=0).to(dev), dq=torch.empty_like(q),
+                       dk=torch.empty_like(k), dv=torch.empty_like(v),
+                       ws=torch.empty(max(16, need), dtype=torch.uint8, device=dev))
+            flops = 2.5 * flops
+            nbytes = backward_bytes(w)
         if args.tune and not split and not paged:
             cfg, tms = fa.attn_fwd_autotune(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
                                             w.scale, dt, reps=10)
             plan = fa.attn_fwd_plan_ex(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dt, cfg)
             plan["tuning_ms"] = {str(i): round(t, 5) for i, t in tms.items()}
         runs.append(dict(w=w, q=q, k=k, v=v, o=o, lse=lse, plan=plan, split=split, ws=ws, dt=dt, paged=paged, cfg=cfg,
-                         flops=flops, bytes=nbytes, hbm_bound=flops / nbytes < RIDGE))
+                         flops=flops, bytes=nbytes, hbm_bound=flops / nbytes < RIDGE, bwd=bwd))
 
     def launch(r):
         # the current stream is torch's capture stream while a graph is recorded
         w = r["w"]
         s = torch.cuda.current_stream(dev).cuda_stream
-        if r["paged"]:
+        if r["bwd"]:
+            bd = r["bwd"]
+            fa.attn_bwd(r["q"], r["k"], r["v"], r["o"], bd["do"], r["lse"], bd["dq"], bd["dk"], bd["dv"], w.B, w.Hq,
+                        w.Hkv, w.N, w.d, w.causal, w.window, w.scale, r["dt"], bd["ws"], bd["ws"].numel(), s)
+        elif r["paged"]:
             pg = r["paged"]
             fa.attn_fwd_paged_ex(r["q"], r["k"], r["v"], pg["bt"], pg["sl"], r["o"], r["lse"], w.B, w.Hq, w.Hkv,
                                  w.N, w.d, pg["ps"], pg["num_pages"], pg["max_pages"], w.nk, w.causal, w.window,
@@ -433,7 +503,8 @@ def main() -> int:
                         "plan": r["plan"]})
 
     result = {
-        "metric": "attention fwd TFLOP/s (4*B*Hq*N^2*d, x1/2 causal) & % of MI355X MFMA peak",
+        "metric": ("attention bwd TFLOP/s (10*B*Hq*N^2*d, x1/2 causal) & % of MI355X MFMA peak" if args.backward
+                   else "attention fwd TFLOP/s (4*B*Hq*N^2*d, x1/2 causal) & % of MI355X MFMA peak"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -460,16 +531,19 @@ def main() -> int:
             "peak": roof["peak"],
             "unit": roof["unit"],
             "frac": round(roof["achieved"] / roof["peak"], 4),
-            "traffic": traffic_from_profiles(label(runs[dom])),
+            "traffic": traffic_from_profiles(label(runs[dom]), "bwd" if args.backward else "fwd"),
             **({"algorithmic_bytes": roof["algorithmic_bytes"]} if "algorithmic_bytes" in roof else {}),
         },
         "kernels": kernels,
         "frac_of_peak_whole_step": round(value / PEAK_TFLOPS[wls[0].dtype], 4),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 5),
-        "kernel_source_sha": kernel_source_hash(),
+        "kernel_source_sha": kernel_source_hash("bwd" if args.backward else "fwd"),
     }
+    if args.backward:
+        result["config"]["pass"] = "backward"
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wls, args.cpu_budget)
+        result["cpu_baseline"] = (cpu_baseline_backward(wls, args.cpu_budget) if args.backward
+                                  else cpu_baseline(wls, args.cpu_budget))
     print(json.dumps(result), flush=True)
     return 0
 

@@ -156,8 +156,11 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dK and dV: one workgroup per (batch, K/V head, BN = 32 * NW keys).
+// At d = 64 the register budget of two waves per SIMD is enough; asking for
+// it lets two workgroups share a compute unit.
 template <int D, int DT, int MASK, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
     constexpr int BN = 32 * NW;
     constexpr int BM = 64;                  // query rows per step
     constexpr int KT = D / 16;
@@ -462,7 +465,6 @@ namespace {
 
 using attnbwd::BwdParams;
 
-constexpr int kNW = 4;                       // waves per workgroup, both main kernels
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
 
@@ -485,25 +487,60 @@ int check_bwd_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, in
     return ATTN_OK;
 }
 
-template <int D, int DT, int MASK>
-hipError_t launch_main(const BwdParams &p, int64_t grid_kv, int64_t grid_q, int64_t grid_pre, hipStream_t st) {
-    hipLaunchKernelGGL((attnbwd::attn_bwd_pre_kernel<D, DT>), dim3((unsigned)grid_pre), dim3(256), 0, st, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((attnbwd::attn_bwd_dkdv_kernel<D, DT, MASK, kNW>), dim3((unsigned)grid_kv), dim3(kNW * 64), 0,
-                       st, p);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((attnbwd::attn_bwd_dq_kernel<D, DT, MASK, kNW>), dim3((unsigned)grid_q), dim3(kNW * 64), 0,
-                       st, p);
+// Waves per workgroup of the two main kernels, chosen per call (measured):
+// 4 (128 keys or query rows per workgroup), except for masked runs whose
+// 128-wide grid has fewer than two workgroups per compute unit: there 2
+// (64 wide) halves the longest workgroup, which sets the time of a causal
+// run on a small grid (lab N = 4096 causal: 0.257 -> 0.217 ms).  Unmasked
+// small grids stay at 4 (lab N = 4096: 0.232 ms at 4, 0.271 ms at 2).
+struct Plan {
+    int nw_kv, nw_q;
+    int64_t grid_kv, grid_q, grid_pre;
+};
+
+template <int D, int DT, int MASK, int NW>
+hipError_t launch_dkdv(const BwdParams &p, int64_t grid, hipStream_t st) {
+    hipLaunchKernelGGL((attnbwd::attn_bwd_dkdv_kernel<D, DT, MASK, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+                       p);
     return hipGetLastError();
 }
 
+template <int D, int DT, int MASK, int NW>
+hipError_t launch_dq(const BwdParams &p, int64_t grid, hipStream_t st) {
+    hipLaunchKernelGGL((attnbwd::attn_bwd_dq_kernel<D, DT, MASK, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int D, int DT, int MASK>
+hipError_t launch_main(const BwdParams &p, const Plan &pl, hipStream_t st) {
+    hipLaunchKernelGGL((attnbwd::attn_bwd_pre_kernel<D, DT>), dim3((unsigned)pl.grid_pre), dim3(256), 0, st, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = pl.nw_kv == 4 ? launch_dkdv<D, DT, MASK, 4>(p, pl.grid_kv, st) : launch_dkdv<D, DT, MASK, 2>(p, pl.grid_kv, st);
+    if (err != hipSuccess) return err;
+    return pl.nw_q == 4 ? launch_dq<D, DT, MASK, 4>(p, pl.grid_q, st) : launch_dq<D, DT, MASK, 2>(p, pl.grid_q, st);
+}
+
 template <int D, int DT>
-hipError_t launch_mask(int mask, const BwdParams &p, int64_t gk, int64_t gq, int64_t gp, hipStream_t st) {
-    if (mask == attnfwd::MASK_NONE) return launch_main<D, DT, attnfwd::MASK_NONE>(p, gk, gq, gp, st);
-    if (mask == attnfwd::MASK_CAUSAL) return launch_main<D, DT, attnfwd::MASK_CAUSAL>(p, gk, gq, gp, st);
-    return launch_main<D, DT, attnfwd::MASK_WINDOW>(p, gk, gq, gp, st);
+hipError_t launch_mask(int mask, const BwdParams &p, const Plan &pl, hipStream_t st) {
+    if (mask == attnfwd::MASK_NONE) return launch_main<D, DT, attnfwd::MASK_NONE>(p, pl, st);
+    if (mask == attnfwd::MASK_CAUSAL) return launch_main<D, DT, attnfwd::MASK_CAUSAL>(p, pl, st);
+    return launch_main<D, DT, attnfwd::MASK_WINDOW>(p, pl, st);
+}
+
+constexpr int64_t kMinWorkgroups = 512;   // two per compute unit
+
+Plan make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int mask) {
+    Plan pl;
+    const int64_t kv4 = B * Hkv * ((N + 127) / 128), q4 = B * Hq * ((N + 127) / 128);
+    const bool masked = mask != attnfwd::MASK_NONE;
+    pl.nw_kv = (masked && kv4 < kMinWorkgroups) ? 2 : 4;
+    pl.nw_q = (masked && q4 < kMinWorkgroups) ? 2 : 4;
+    pl.grid_kv = B * Hkv * ((N + 32 * pl.nw_kv - 1) / (32 * pl.nw_kv));
+    pl.grid_q = B * Hq * ((N + 32 * pl.nw_q - 1) / (32 * pl.nw_q));
+    const int64_t rows_per_block = 256 / (d / 8);
+    pl.grid_pre = (B * Hq * padded_rows(N) + rows_per_block - 1) / rows_per_block;
+    return pl;
 }
 
 int bwd_status(hipError_t err) {
@@ -574,23 +611,17 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
     p.window = mask == attnfwd::MASK_WINDOW ? (int)std::min<int64_t>(window, N) : 0;
     p.n_bh = (int)(B * Hq);
     p.n_bhk = (int)(B * Hkv);
-    constexpr int bmq = 32 * kNW, bnk = 32 * kNW;
-    p.n_qtiles = (int)((N + bmq - 1) / bmq);
+    const Plan pl = make_plan(B, Hq, Hkv, N, d, mask);
+    p.n_qtiles = (int)((N + 32 * pl.nw_q - 1) / (32 * pl.nw_q));
     p.c2 = (float)((double)scale * 1.4426950408889634);
     p.scale = scale;
-    const int64_t grid_kv = B * Hkv * ((N + bnk - 1) / bnk);
-    const int64_t grid_q = B * Hq * (int64_t)p.n_qtiles;
-    const int64_t rows_per_block = 256 / (d / 8);
-    const int64_t grid_pre = (B * Hq * p.Npad + rows_per_block - 1) / rows_per_block;
-    if (grid_kv > INT_MAX || grid_q > INT_MAX || grid_pre > INT_MAX) return ATTN_ERR_SHAPE;
+    if (pl.grid_kv > INT_MAX || pl.grid_q > INT_MAX || pl.grid_pre > INT_MAX) return ATTN_ERR_SHAPE;
     hipStream_t st = (hipStream_t)stream;
     hipError_t err;
     if (d == 64)
-        err = dtype == ATTN_F16 ? launch_mask<64, 0>(mask, p, grid_kv, grid_q, grid_pre, st)
-                                : launch_mask<64, 1>(mask, p, grid_kv, grid_q, grid_pre, st);
+        err = dtype == ATTN_F16 ? launch_mask<64, 0>(mask, p, pl, st) : launch_mask<64, 1>(mask, p, pl, st);
     else
-        err = dtype == ATTN_F16 ? launch_mask<128, 0>(mask, p, grid_kv, grid_q, grid_pre, st)
-                                : launch_mask<128, 1>(mask, p, grid_kv, grid_q, grid_pre, st);
+        err = dtype == ATTN_F16 ? launch_mask<128, 0>(mask, p, pl, st) : launch_mask<128, 1>(mask, p, pl, st);
     return bwd_status(err);
 }
 
