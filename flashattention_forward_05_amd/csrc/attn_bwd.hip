@@ -62,6 +62,8 @@ struct BwdParams {
     int window;          // > 0 only with MASK_WINDOW
     int n_bh;            // B * Hq
     int n_bhk;           // B * Hkv
+    int hsplit;          // dK/dV: query heads of a group split over this many workgroups
+    float *ws_dkv;       // hsplit > 1: fp32 partial dk (scaled) and dv, 2 x (hsplit, B * Hkv, N, D)
     int n_qtiles;        // dq kernel: query tiles per head
     float c2;            // scale * log2(e)
     float scale;
@@ -176,7 +178,10 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     const int N = p.N;
     const int bid = blockIdx.x;
     const int bhk = bid % p.n_bhk;
-    const int kt = bid / p.n_bhk;           // key tiles in ascending order: most visible queries first
+    const int rest = bid / p.n_bhk;
+    const int hs = rest % p.hsplit;         // which share of the group's query heads
+    const int kt = rest / p.hsplit;         // key tiles in ascending order: most visible queries first
+    const int gper = p.group / p.hsplit;
     const int b = bhk / p.Hkv;
     const int hk = bhk - b * p.Hkv;
     const int j0 = kt * BN;
@@ -208,10 +213,10 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     if constexpr (MASK != MASK_NONE) qt_begin = j0 / BM;
     if constexpr (MASK == MASK_WINDOW) qt_end = min(qt_end, (j0 + BN - 1 + p.window - 1) / BM + 1);
     const int nq = max(qt_end - qt_begin, 0);
-    const int nsteps = nq * p.group;
+    const int nsteps = nq * gper;
 
     auto issue = [&](int s) {
-        const int h = hk * p.group + s / nq;
+        const int h = hk * p.group + hs * gper + s / nq;
         const int i0 = (qt_begin + s % nq) * BM;
         const int64_t bh = (int64_t)b * p.Hq + h;
         load_rows<D, NW, BM>(p.q + bh * N * D, i0, N, qs[s & 1], wave, lane);
@@ -300,7 +305,22 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     }
 
     // lane: key mykey, register r: channel 32 cb + 8 (r / 4) + 4 g + r % 4
-    if (mykey < N) {
+    if (mykey < N && p.hsplit > 1) {
+        // partial sums over this share of the heads, reduced by attn_bwd_dkv_reduce_kernel
+        const int64_t part = (int64_t)p.hsplit * p.n_bhk * N * D;
+        float *dkr = p.ws_dkv + (((int64_t)hs * p.n_bhk + bhk) * N + mykey) * D;
+        float *dvr = dkr + part;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int ch = 32 * cb + 8 * rq + 4 * g;
+                *(float4 *)(dkr + ch) = make_float4(p.scale * dka[cb][4 * rq], p.scale * dka[cb][4 * rq + 1],
+                                                    p.scale * dka[cb][4 * rq + 2], p.scale * dka[cb][4 * rq + 3]);
+                *(float4 *)(dvr + ch) =
+                    make_float4(dva[cb][4 * rq], dva[cb][4 * rq + 1], dva[cb][4 * rq + 2], dva[cb][4 * rq + 3]);
+            }
+    } else if (mykey < N) {
         uint16_t *dkr = p.dk + ((int64_t)bhk * N + mykey) * D;
         uint16_t *dvr = p.dv + ((int64_t)bhk * N + mykey) * D;
 #pragma unroll
@@ -316,6 +336,27 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
                 *(u32x2 *)(dvr + ch) = wv;
             }
     }
+}
+
+// ---------------------------------------------------------------------------
+// With split heads: dk / dv = sum of the hsplit fp32 partials, rounded once.
+// Four channels per thread; blockIdx.y selects dk (0) or dv (1).
+template <int DT>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_reduce_kernel(BwdParams p, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index over (B * Hkv, N, D)
+    if (i >= n4) return;
+    const int64_t part4 = (int64_t)p.hsplit * n4;                // float4s of one tensor's partials
+    const float4 *src = (const float4 *)p.ws_dkv + blockIdx.y * part4 + i;
+    float4 acc = src[0];
+    for (int h = 1; h < p.hsplit; ++h) {
+        const float4 t = src[h * n4];
+        acc.x += t.x;
+        acc.y += t.y;
+        acc.z += t.z;
+        acc.w += t.w;
+    }
+    uint16_t *dst = (blockIdx.y == 0 ? p.dk : p.dv) + 4 * i;
+    *(u32x2 *)dst = u32x2{pack2<DT>(acc.x, acc.y), pack2<DT>(acc.z, acc.w)};
 }
 
 // ---------------------------------------------------------------------------
@@ -470,6 +511,28 @@ constexpr int64_t kMaxHeads = int64_t(1) << 24;
 
 int64_t padded_rows(int64_t N) { return (N + 63) / 64 * 64; }
 
+// Query heads of a K/V group split over this many dK/dV workgroups: with few
+// K/V heads (MQA) the group's heads would otherwise run one after another in
+// few, long workgroups.  Aim for 2048 workgroups of 128 keys; the split
+// divides G.  Depends on the shape only, so the workspace size does too.
+int64_t head_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t N) {
+    const int64_t G = Hq / Hkv;
+    const int64_t grid4 = B * Hkv * ((N + 127) / 128);
+    if (grid4 <= 0) return 1;
+    int64_t want = grid4 >= 2048 ? 1 : (2048 + grid4 - 1) / grid4;
+    want = std::min(want, G);
+    while (want > 1 && G % want != 0) --want;
+    return std::max<int64_t>(want, 1);
+}
+
+// Workspace: per-row {D, lse log2 e} (B * Hq * Npad float2), then from a
+// 256-byte boundary the fp32 partial dk and dv of split heads.
+int64_t dl_bytes(int64_t B, int64_t Hq, int64_t N) { return (B * Hq * padded_rows(N) * 8 + 255) / 256 * 256; }
+int64_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
+    const int64_t hs = head_split(B, Hq, Hkv, N);
+    return dl_bytes(B, Hq, N) + (hs > 1 ? 2 * hs * B * Hkv * N * d * 4 : 0);
+}
+
 bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
@@ -494,7 +557,7 @@ int check_bwd_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, in
 // run on a small grid (lab N = 4096 causal: 0.257 -> 0.217 ms).  Unmasked
 // small grids stay at 4 (lab N = 4096: 0.232 ms at 4, 0.271 ms at 2).
 struct Plan {
-    int nw_kv, nw_q;
+    int nw_kv, nw_q, hsplit;
     int64_t grid_kv, grid_q, grid_pre;
 };
 
@@ -518,6 +581,13 @@ hipError_t launch_main(const BwdParams &p, const Plan &pl, hipStream_t st) {
     if (err != hipSuccess) return err;
     err = pl.nw_kv == 4 ? launch_dkdv<D, DT, MASK, 4>(p, pl.grid_kv, st) : launch_dkdv<D, DT, MASK, 2>(p, pl.grid_kv, st);
     if (err != hipSuccess) return err;
+    if (pl.hsplit > 1) {
+        const int64_t n4 = (int64_t)p.n_bhk * p.N * D / 4;
+        hipLaunchKernelGGL((attnbwd::attn_bwd_dkv_reduce_kernel<DT>), dim3((unsigned)((n4 + 255) / 256), 2), dim3(256),
+                           0, st, p, n4);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     return pl.nw_q == 4 ? launch_dq<D, DT, MASK, 4>(p, pl.grid_q, st) : launch_dq<D, DT, MASK, 2>(p, pl.grid_q, st);
 }
 
@@ -532,11 +602,12 @@ constexpr int64_t kMinWorkgroups = 512;   // two per compute unit
 
 Plan make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int mask) {
     Plan pl;
-    const int64_t kv4 = B * Hkv * ((N + 127) / 128), q4 = B * Hq * ((N + 127) / 128);
+    pl.hsplit = (int)head_split(B, Hq, Hkv, N);
+    const int64_t kv4 = B * Hkv * ((N + 127) / 128) * pl.hsplit, q4 = B * Hq * ((N + 127) / 128);
     const bool masked = mask != attnfwd::MASK_NONE;
     pl.nw_kv = (masked && kv4 < kMinWorkgroups) ? 2 : 4;
     pl.nw_q = (masked && q4 < kMinWorkgroups) ? 2 : 4;
-    pl.grid_kv = B * Hkv * ((N + 32 * pl.nw_kv - 1) / (32 * pl.nw_kv));
+    pl.grid_kv = B * Hkv * ((N + 32 * pl.nw_kv - 1) / (32 * pl.nw_kv)) * pl.hsplit;
     pl.grid_q = B * Hq * ((N + 32 * pl.nw_q - 1) / (32 * pl.nw_q));
     const int64_t rows_per_block = 256 / (d / 8);
     pl.grid_pre = (B * Hq * padded_rows(N) + rows_per_block - 1) / rows_per_block;
@@ -556,7 +627,7 @@ extern "C" {
 
 int64_t attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
     if (check_bwd_sizes(B, Hq, Hkv, N, d, 0, 0, 1.0f, ATTN_F16) != ATTN_OK) return -1;
-    return B * Hq * padded_rows(N) * 8;
+    return workspace_bytes_for(B, Hq, Hkv, N, d);
 }
 
 int attn_bwd_validate(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -567,7 +638,7 @@ int attn_bwd_validate(const void *q, const void *k, const void *v, const void *o
     if (rc != ATTN_OK) return rc;
     if (N == 0) return ATTN_OK;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ATTN_ERR_NULL;
-    if (workspace_bytes < B * Hq * padded_rows(N) * 8) return ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < workspace_bytes_for(B, Hq, Hkv, N, d)) return ATTN_ERR_WORKSPACE;
     const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
                           (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace;
     if ((mis & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_ALIGN;
@@ -611,7 +682,10 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
     p.window = mask == attnfwd::MASK_WINDOW ? (int)std::min<int64_t>(window, N) : 0;
     p.n_bh = (int)(B * Hq);
     p.n_bhk = (int)(B * Hkv);
+    p.hsplit = 1;
+    p.ws_dkv = (float *)((char *)workspace + dl_bytes(B, Hq, N));
     const Plan pl = make_plan(B, Hq, Hkv, N, d, mask);
+    p.hsplit = pl.hsplit;
     p.n_qtiles = (int)((N + 32 * pl.nw_q - 1) / (32 * pl.nw_q));
     p.c2 = (float)((double)scale * 1.4426950408889634);
     p.scale = scale;

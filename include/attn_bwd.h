@@ -36,7 +36,10 @@
  * attn_bwd_workspace_size(...) bytes, 16-byte aligned, that nothing else
  * uses while the call runs; the library allocates nothing and keeps no
  * state, so calls on distinct streams with distinct workspaces are safe.
- * Its contents are scratch (per-row D and lse) and are overwritten.
+ * Its contents are scratch and are overwritten: per query row D and the
+ * lse in base 2, and, for shapes with few K/V heads (MQA), where the query
+ * heads of a group are split over several workgroups, their fp32 partial
+ * dk and dv (summed by a fourth kernel).
  *
  * Errors (host-side, before anything is enqueued; outputs untouched):
  *   the shape, d, dtype, mask and scale rules of attn_fwd_validate;
@@ -46,7 +49,7 @@
  *   or lse not 4-byte aligned;
  *   ATTN_ERR_ALIAS when dq, dk, dv or the workspace overlap an input or each
  *   other.
- * N == 0 is a no-op returning ATTN_OK.  attn_bwd enqueues three kernels on
+ * N == 0 is a no-op returning ATTN_OK.  attn_bwd enqueues three (or four) kernels on
  * `stream` (NULL = default) and never synchronises; device faults surface at
  * the caller's next synchronisation.
  */
@@ -60,7 +63,10 @@ extern "C" {
 #endif
 
 /* Bytes of workspace attn_bwd needs: 8 bytes per query row, rows padded to
- * a multiple of 64 per head.  -1 for shapes attn_bwd would reject. */
+ * a multiple of 64 per head (rounded up to 256 bytes), plus 2 * S * B * Hkv
+ * * N * d * 4 bytes when the query heads of a K/V group are split S > 1
+ * ways (S divides Hq / Hkv and is chosen from the shape: S > 1 only when
+ * B * Hkv * ceil(N / 128) < 2048).  -1 for shapes attn_bwd would reject. */
 int64_t attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
 
 /* Host-side checks only (no HIP call); the status attn_bwd would return

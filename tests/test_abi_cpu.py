@@ -258,7 +258,7 @@ def test_autotune_rejects_before_touching_the_gpu():
 
 # ---- backward (include/attn_bwd.h)
 BG = dict(q=A, k=2 * A, v=3 * A, o=4 * A, dout=5 * A, lse=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
-          B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, window=0, scale=0.125, dtype=0, ws=10 * A, wsb=1 << 16)
+          B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, window=0, scale=0.125, dtype=0, ws=10 * A, wsb=1 << 19)
 
 
 def validate_bwd(**over):
@@ -279,20 +279,28 @@ def validate_bwd(**over):
     ({"scale": float("nan")}, 4),
     ({"q": A + 8}, 5), ({"dk": 8 * A + 4}, 5), ({"ws": 10 * A + 8}, 5), ({"lse": 6 * A + 2}, 5),
     ({"dq": A}, 6), ({"dk": 5 * A + 16}, 6), ({"dv": 8 * A}, 6), ({"ws": 6 * A}, 6), ({"ws": 9 * A + 32}, 6),
-    ({"wsb": 2 * 4 * 128 * 8 - 1}, 9),
+    ({"wsb": 2 * 4 * 128 * 8 + 2 * 2 * 2 * 2 * 100 * 64 * 4 - 1}, 9),
 ])
 def test_bwd_validate_codes(over, code):
     assert validate_bwd(**over) == code
 
 
 def test_bwd_workspace_size():
-    # 8 bytes per query row, rows padded to a multiple of 64 per head
-    assert fa.attn_bwd_workspace_size(2, 4, 2, 100, 64) == 2 * 4 * 128 * 8
-    assert fa.attn_bwd_workspace_size(1, 1, 1, 64, 128) == 64 * 8
+    # 8 bytes per query row, rows padded to a multiple of 64 per head, rounded
+    # to 256 bytes; plus fp32 partial dk and dv when the heads are split
+    assert fa.attn_bwd_workspace_size(2, 4, 4, 100, 64) == 2 * 4 * 128 * 8          # G = 1: no split
+    assert fa.attn_bwd_workspace_size(1, 1, 1, 64, 128) == 512
     assert fa.attn_bwd_workspace_size(1, 1, 1, 0, 128) == 0
+    assert fa.attn_bwd_workspace_size(4, 32, 8, 8192, 128) == 4 * 32 * 8192 * 8     # 2048 workgroups: no split
+    # MQA, N = 32768: 256 workgroups of 128 keys -> the 32 query heads split 8 ways
+    assert fa.attn_bwd_workspace_size(1, 32, 1, 32768, 128) == 32 * 32768 * 8 + 2 * 8 * 32768 * 128 * 4
+    # G = 3 and a wish of 2048 / 1 workgroups: the largest divisor of 3, i.e. 3
+    assert fa.attn_bwd_workspace_size(1, 3, 1, 100, 64) == 3 * 128 * 8 + 2 * 3 * 100 * 64 * 4
     assert fa.attn_bwd_workspace_size(1, 3, 2, 64, 64) == -1
     assert fa.attn_bwd_workspace_size(1, 1, 1, 64, 96) == -1
-    assert validate_bwd(wsb=2 * 4 * 128 * 8) == 0
+    # B=2, Hq=4, Hkv=2, N=100: 2 workgroups of 128 keys -> split G = 2 ways
+    assert fa.attn_bwd_workspace_size(2, 4, 2, 100, 64) == 2 * 4 * 128 * 8 + 2 * 2 * 2 * 2 * 100 * 64 * 4
+    assert validate_bwd(wsb=2 * 4 * 128 * 8 + 2 * 2 * 2 * 2 * 100 * 64 * 4) == 0
 
 
 def test_bwd_rejects_before_touching_the_gpu():
