@@ -20,7 +20,7 @@ using attnfwd::Params;
 
 // Tile configurations compiled into the library.  qb: 32-row query blocks
 // per wave; nwq: query waves per workgroup; ksplit: key groups per workgroup
-// (2 = a second set of waves takes the second half of the key range, merged
+// (2 or 4 = further sets of waves take later parts of the key range, merged
 // in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring (of
 // each of the K and V rings for kind 2); kind: 0 = lockstep kernel, 1 =
 // ping-pong (the two wave groups alternate matrix and vector phases; then
@@ -32,7 +32,7 @@ struct TileCfg {
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 9;
+constexpr int kNumConfigs = 10;
 constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
     {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
@@ -43,6 +43,7 @@ constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 1, 64, 3, 2},   // 6: pipelined, 128 rows, 4 waves
     {1, 2, 2, 64, 2, 0},   // 7: 64 rows, 4 waves (two key groups), two workgroups per CU
     {1, 1, 1, 64, 3, 0},   // 8: 32 rows, 1 wave (few query rows: decoding)
+    {1, 1, 4, 64, 2, 0},   // 9: 32 rows, 4 waves in four key groups (small grids)
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},
@@ -54,6 +55,7 @@ constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 1, 32, 3, 2},
     {1, 2, 2, 32, 2, 0},
     {1, 1, 1, 32, 3, 0},
+    {1, 1, 4, 32, 2, 0},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
@@ -93,13 +95,17 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int ca
 // d = 128 shapes run 128-row workgroups with two key groups (1).  For d = 64,
 // 64-row workgroups, two per compute unit (7), win on small grids and on
 // masked runs, where they spread the uneven causal work over twice as many
-// workgroups; larger unmasked grids keep the 128-row workgroups (1).
+// workgroups; larger unmasked grids keep the 128-row workgroups (1).  When
+// even 32-row workgroups are at most one per compute unit, 32 rows with four
+// key groups (9) keep every SIMD busy (lab N = 1024: 183 -> 231 TFLOP/s
+// unmasked, 88 -> 112 causal).
 int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask) {
     const int64_t wg128 = B * Hq * ((N + 127) / 128);
     if (d == 128) {
         const int64_t wg256 = B * Hq * ((N + 255) / 256);
         return wg256 >= 512 ? 2 : 1;
     }
+    if (B * Hq * ((N + 31) / 32) <= 256) return 9;
     if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 7 : 1;
     return wg128 < 128 ? 7 : 1;
 }
@@ -267,11 +273,13 @@ KvView kv_view(int64_t Hq, int64_t Hkv, int64_t Nq) {
 // rows, many K/V heads, so many workgroups); at 32 rows and more, with few
 // K/V heads (MQA decoding), the 8-wave workgroups of configuration 1 keep
 // more loads in flight per compute unit; longer query blocks take the choice
-// of the plain forward.
+// of the plain forward, with 64-row workgroups (7) in place of the four-key-
+// group ones (9): key chunks already spread a small grid.
 int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask) {
     if (Nq < 32) return 8;
     if (Nq <= 128) return 1;
-    return auto_config(B, Hq, Nq, d, mask);
+    const int id = auto_config(B, Hq, Nq, d, mask);
+    return id == 9 ? 7 : id;
 }
 
 struct SplitPlan {

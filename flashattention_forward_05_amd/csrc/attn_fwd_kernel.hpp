@@ -1,9 +1,9 @@
 // attn_fwd_kernel.hpp -- fused exact attention forward for gfx950 (MI355X).
 //
 // One workgroup computes one (batch, query head, query tile) of BM rows.  Its
-// NWQ query waves each own QB blocks of 32 query rows; with KSPLIT = 2 a
-// second set of NWQ waves owns the same rows and takes the second half of the
-// key range, and the two partial results are merged in LDS at the end (the
+// NWQ query waves each own QB blocks of 32 query rows; with KSPLIT = 2 or 4,
+// further sets of NWQ waves own the same rows and take later parts of the
+// key range, and the partial results are merged in LDS at the end (the
 // rescale-and-add of partial softmax results that "Optimizaciones de
 // Atencion", section "FlashDecoding", uses to combine key chunks).  A wave
 // walks its key/value tiles (BN keys each) keeping a running row max, running
@@ -71,7 +71,7 @@ struct Kernel {
     static constexpr int STAGEB = KSPLIT * TILEB;                      // one stage of K (or V), all groups
     static_assert((BN * CHUNKS_PER_ROW) % (64 * NWQ) == 0, "tile must split evenly over the waves");
     static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
-    static_assert(NSTAGE >= 2 && NSTAGE <= 4 && (KSPLIT == 1 || KSPLIT == 2), "unsupported pipeline");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4 && (KSPLIT == 1 || KSPLIT == 2 || KSPLIT == 4), "unsupported pipeline");
 
     // per-wave state
     struct State {
@@ -459,9 +459,11 @@ struct Kernel {
         else
             loop<false>(x, st, half, my_begin, my_count);
 
-        // ---- merge the key groups: group 1 hands (m, l, O) to group 0.  The
-        // ring is idle now; channel block cb of O goes to ring array cb.
-        if constexpr (KSPLIT == 2) {
+        // ---- merge the key groups: groups 1 .. KSPLIT-1 hand (m, l, O) to
+        // group 0.  The ring is idle now; channel block cb of O of group g
+        // goes to ring array cb at slot g - 1.
+        if constexpr (KSPLIT > 1) {
+            constexpr int SLOT = NWQ * QB * 16 * 64;   // floats of one group's channel block
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             __syncthreads();
             char *ring[2 * NSTAGE];
@@ -470,39 +472,56 @@ struct Kernel {
                 ring[2 * s2] = x.kst[s2];
                 ring[2 * s2 + 1] = x.vst[s2];
             }
-            if (x.kgroup == 1) {
+            if (x.kgroup != 0) {
+                const int slot = x.kgroup - 1;
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     const int base = (x.wave_q * QB + qb);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
-                        float *dst = (float *)ring[cb];
+                        float *dst = (float *)ring[cb] + slot * SLOT;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) dst[(base * 16 + r) * 64 + x.lane] = st.oacc[qb][cb][r];
                     }
-                    ml[(base * 2 + 0) * 64 + x.lane] = st.mrun[qb];
-                    ml[(base * 2 + 1) * 64 + x.lane] = st.lsum[qb];
+                    ml[((slot * NWQ * QB + base) * 2 + 0) * 64 + x.lane] = st.mrun[qb];
+                    ml[((slot * NWQ * QB + base) * 2 + 1) * 64 + x.lane] = st.lsum[qb];
                 }
             }
             __syncthreads();
-            if (x.kgroup == 1) return;
+            if (x.kgroup != 0) return;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int base = (x.wave_q * QB + qb);
-                const float m1 = ml[(base * 2 + 0) * 64 + x.lane];
-                const float l1 = ml[(base * 2 + 1) * 64 + x.lane];
-                const float m0 = st.mrun[qb];
-                const float m = fmaxf(m0, m1);
-                const float a0 = (m0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
-                const float a1 = (m1 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+                float mg[KSPLIT], lg[KSPLIT];
+                mg[0] = st.mrun[qb];
+                lg[0] = st.lsum[qb];
+                float m = mg[0];
+#pragma unroll
+                for (int g2 = 1; g2 < KSPLIT; ++g2) {
+                    mg[g2] = ml[(((g2 - 1) * NWQ * QB + base) * 2 + 0) * 64 + x.lane];
+                    lg[g2] = ml[(((g2 - 1) * NWQ * QB + base) * 2 + 1) * 64 + x.lane];
+                    m = fmaxf(m, mg[g2]);
+                }
+                float a[KSPLIT];
+                float l = 0.0f;
+#pragma unroll
+                for (int g2 = 0; g2 < KSPLIT; ++g2) {
+                    a[g2] = (mg[g2] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mg[g2] - m);
+                    l += lg[g2] * a[g2];
+                }
                 st.mrun[qb] = m;
-                st.lsum[qb] = st.lsum[qb] * a0 + l1 * a1;
+                st.lsum[qb] = l;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     const float *src = (const float *)ring[cb];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        st.oacc[qb][cb][r] = st.oacc[qb][cb][r] * a0 + src[(base * 16 + r) * 64 + x.lane] * a1;
+                    for (int r = 0; r < 16; ++r) {
+                        float acc = st.oacc[qb][cb][r] * a[0];
+#pragma unroll
+                        for (int g2 = 1; g2 < KSPLIT; ++g2)
+                            acc += src[(g2 - 1) * SLOT + (base * 16 + r) * 64 + x.lane] * a[g2];
+                        st.oacc[qb][cb][r] = acc;
+                    }
                 }
             }
         }
@@ -579,10 +598,10 @@ __global__ __launch_bounds__(NWQ * KSPLIT * 64) void attn_fwd_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) char v2[NSTAGE > 2 ? SB : 16];
     __shared__ __attribute__((aligned(1024))) char k3[NSTAGE > 3 ? SB : 16];
     __shared__ __attribute__((aligned(1024))) char v3[NSTAGE > 3 ? SB : 16];
-    // the merge of two key groups keeps O in the ring and (m, l) here
-    static_assert(KSPLIT == 1 || (D / 32 <= 2 * NSTAGE && NWQ * QB * 16 * 64 * 4 <= SB),
+    // the merge of the key groups keeps O in the ring and (m, l) here
+    static_assert(KSPLIT == 1 || (D / 32 <= 2 * NSTAGE && (KSPLIT - 1) * NWQ * QB * 16 * 64 * 4 <= SB),
                   "ring too small to hold the key-group merge");
-    __shared__ __attribute__((aligned(16))) float ml[KSPLIT == 2 ? NWQ * QB * 2 * 64 : 4];
+    __shared__ __attribute__((aligned(16))) float ml[KSPLIT > 1 ? (KSPLIT - 1) * NWQ * QB * 2 * 64 : 4];
     char *kst[NSTAGE];
     char *vst[NSTAGE];
     kst[0] = k0; vst[0] = v0;

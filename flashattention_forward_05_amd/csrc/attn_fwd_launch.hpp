@@ -14,7 +14,7 @@ namespace attnfwd {
 hipError_t launch_pipelined(int64_t d, int dt, int mask, int cfg, const Params &p, int64_t grid,
                             hipStream_t stream);
 
-// Lockstep-kernel configurations (ids 0, 1, 2, 3, 7, 8) in their own
+// Lockstep-kernel configurations (ids 0, 1, 2, 3, 7, 8, 9) in their own
 // translation units: contiguous K/V at head dim 128, and paged K/V at head
 // dim 64 and 128.
 hipError_t launch_lockstep_d128(int dt, int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream);

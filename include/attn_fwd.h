@@ -229,7 +229,7 @@ int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float
  * R query rows per head as launched -- G * Nq when the heads are stacked, see
  * attn_fwd_splitkv_plan -- configuration 8, one-wave 32-row workgroups, for
  * R < 32; configuration 1 for 32 <= R <= 128; else the choice attn_fwd
- * makes). */
+ * makes, with configuration 7 in place of 9). */
 int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, float *lse,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                         int causal, int64_t window, float scale, int dtype, int64_t num_splits,

@@ -117,13 +117,18 @@ def test_launch_rejects_before_touching_the_gpu():
 
 
 def test_auto_config_choice():
-    """The automatic tile configuration follows the documented rule: 64-row
-    workgroups for d=64 masked runs and small grids, 128-row workgroups for
-    large unmasked d=64 grids, 256-row workgroups for large d=128 grids."""
+    """The automatic tile configuration follows the documented rule: for d=64,
+    32-row workgroups with four key groups when there are at most 256 of
+    them, else 64-row workgroups for masked runs and small grids and 128-row
+    workgroups for large unmasked grids; 256-row workgroups for large d=128
+    grids."""
     auto = lambda *a: fa.attn_fwd_plan_ex(*a, -1)["config_id"]
     assert auto(2, 4, 4, 4096, 64, 1, 0, 0) == 7        # lab, causal
     assert auto(2, 4, 4, 4096, 64, 0, 0, 0) == 1        # lab, full
-    assert auto(2, 4, 4, 1024, 64, 0, 0, 0) == 7        # small grid
+    assert auto(2, 4, 4, 1024, 64, 0, 0, 0) == 9        # small grid: 32 rows, four key groups
+    assert auto(2, 4, 4, 1024, 64, 1, 0, 0) == 9
+    assert auto(2, 4, 4, 256, 64, 1, 0, 0) == 9
+    assert auto(2, 4, 4, 2048, 64, 1, 0, 0) == 7        # 512 32-row workgroups
     assert auto(1, 12, 12, 2048, 64, 0, 0, 0) == 1      # stress, full
     assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 7      # stress, causal
     assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 2      # GQA prefill
@@ -156,7 +161,7 @@ def validate_kv(**over):
     ({"q": None}, 1), ({"workspace": None}, 1),
     ({"Nk": 0}, 2), ({"Nk": -1}, 2), ({"Nq": 4097}, 2), ({"Nk": (1 << 24) + 1}, 2), ({"Hq": 3}, 2),
     ({"d": 96}, 3), ({"config_id": 4}, 3), ({"config_id": 6}, 3), ({"window": 8, "causal": 0}, 3),
-    ({"num_splits": -1}, 4), ({"num_splits": 1025}, 4), ({"config_id": 9}, 4), ({"scale": float("nan")}, 4),
+    ({"num_splits": -1}, 4), ({"num_splits": 1025}, 4), ({"config_id": 10}, 4), ({"scale": float("nan")}, 4),
     ({"workspace": 6 * G + 8}, 5), ({"q": G + 2}, 5),
     ({"o": 2 * G}, 6), ({"workspace": 3 * G}, 6), ({"workspace": 5 * G}, 6), ({"workspace": 4 * G - 64}, 6),
     ({"workspace_bytes": 64}, 9),
