@@ -230,7 +230,7 @@ def summarize_trace(trace_dir: str) -> str:
     rows = _read_csv(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])
     groups = {}
     for r in rows:
-        if "attn_fwd" not in r["Kernel_Name"]:
+        if "attn_" not in r["Kernel_Name"]:
             continue
         key = (r["Kernel_Name"], int(r["Grid_Size"]) if "Grid_Size" in r else int(r.get("Grid_Size_X", 0)))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -311,7 +311,7 @@ def main() -> int:
     if args.summarize_counters:
         vals = summarize_counters({d: d for d in args.summarize_counters})
         for (k, c), v in sorted(vals.items()):
-            if "attn_fwd" in k:
+            if "attn_" in k:
                 print(f"{k} | {c} | {v:.6g}")
         return 0
     if args.traffic:
