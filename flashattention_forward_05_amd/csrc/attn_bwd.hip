@@ -360,19 +360,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_reduce_kernel(BwdParams p, i
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per (batch, query head, 32 * NW query rows).
-template <int D, int DT, int MASK, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
+// dQ: one workgroup per (batch, query head, 32 * NW query rows).  With KG = 2
+// a second set of NW waves owns the same rows and takes the second half of
+// the key tiles (its own K/V ring); the two partial dQ are summed in LDS at
+// the end.  That doubles the waves of a small grid.
+template <int D, int DT, int MASK, int NW, int KG>
+__global__ __launch_bounds__(NW * KG * 64) void attn_bwd_dq_kernel(BwdParams p) {
     constexpr int BMQ = 32 * NW;
     constexpr int BN = 64;                  // keys per tile
     constexpr int KT = D / 16;
     constexpr int CB = D / 32;
     constexpr int TILEB = BN * D * 2;
-    __shared__ __attribute__((aligned(1024))) char ks_[2][TILEB];
-    __shared__ __attribute__((aligned(1024))) char vs_[2][TILEB];
+    static_assert(KG == 1 || KG == 2, "one or two key groups");
+    static_assert(KG == 1 || NW * CB * 16 * 64 * 4 <= 2 * KG * TILEB, "K ring too small for the dQ merge");
+    __shared__ __attribute__((aligned(1024))) char ks_[2][KG * TILEB];
+    __shared__ __attribute__((aligned(1024))) char vs_[2][KG * TILEB];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wave_all % NW;         // query rows of the wave
+    const int kg = wave_all / NW;           // its key group
     const int g = lane >> 5, l32 = lane & 31;
     const int N = p.N;
     const int bid = blockIdx.x;
@@ -419,19 +426,25 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
     const uint16_t *kh = p.k + bhk * N * D;
     const uint16_t *vh = p.v + bhk * N * D;
     const int wlast = min(iw + 31, N - 1);   // the wave's last valid row
+    // this key group's tiles: [my_begin, my_begin + my_count); every wave runs
+    // `half` steps so that the workgroup barriers match
+    const int half = (nt + KG - 1) / KG;
+    const int my_begin = kt_begin + kg * half;
+    const int my_count = max(0, min(half, nt - kg * half));
 
     auto issue = [&](int s) {
-        const int jt = (kt_begin + s) * BN;
-        load_rows<D, NW, BN>(kh, jt, N, ks_[s & 1], wave, lane);
-        load_rows<D, NW, BN>(vh, jt, N, vs_[s & 1], wave, lane);
+        const int jt = (my_begin + s) * BN;
+        load_rows<D, NW, BN>(kh, jt, N, ks_[s & 1] + kg * TILEB, wave, lane);
+        load_rows<D, NW, BN>(vh, jt, N, vs_[s & 1] + kg * TILEB, wave, lane);
     };
 
-    if (nt > 0) issue(0);
-    for (int s = 0; s < nt; ++s) {
+    if (my_count > 0) issue(0);
+    for (int s = 0; s < half; ++s) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         block_sync();
-        if (s + 1 < nt) issue(s + 1);
-        const int j0 = (kt_begin + s) * BN;
+        if (s + 1 < my_count) issue(s + 1);
+        if (s >= my_count) continue;
+        const int j0 = (my_begin + s) * BN;
         bool any = iw < N;
         bool edge = j0 + BN > N;
         if constexpr (MASK != MASK_NONE) {
@@ -443,8 +456,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
             edge = edge || (j0 <= wlast - p.window);
         }
         if (!any) continue;
-        const char *kl = ks_[s & 1];
-        const char *vl = vs_[s & 1];
+        const char *kl = ks_[s & 1] + kg * TILEB;
+        const char *vl = vs_[s & 1] + kg * TILEB;
 
         u32x4 dsb[BN / 16];
 #pragma unroll
@@ -481,6 +494,25 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
         for (int kstep = 0; kstep < BN / 16; ++kstep)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) dqa[cb] = mfma32<DT>(tr_frag<D>(kl, kstep, cb, lane), dsb[kstep], dqa[cb]);
+    }
+
+    // key group 1 hands its partial dQ^T to group 0 through the idle K ring
+    if constexpr (KG == 2) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        float *buf = (float *)&ks_[0][0];
+        if (kg == 1) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) buf[((wave * CB + cb) * 16 + r) * 64 + lane] = dqa[cb][r];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dqa[cb][r] += buf[((wave * CB + cb) * 16 + r) * 64 + lane];
     }
 
     // lane: row myq, register r: channel 32 cb + 8 (r / 4) + 4 g + r % 4
@@ -557,7 +589,7 @@ int check_bwd_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, in
 // run on a small grid (lab N = 4096 causal: 0.257 -> 0.217 ms).  Unmasked
 // small grids stay at 4 (lab N = 4096: 0.232 ms at 4, 0.271 ms at 2).
 struct Plan {
-    int nw_kv, nw_q, hsplit;
+    int nw_kv, nw_q, kg_q, hsplit;
     int64_t grid_kv, grid_q, grid_pre;
 };
 
@@ -568,9 +600,10 @@ hipError_t launch_dkdv(const BwdParams &p, int64_t grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D, int DT, int MASK, int NW>
+template <int D, int DT, int MASK, int NW, int KG>
 hipError_t launch_dq(const BwdParams &p, int64_t grid, hipStream_t st) {
-    hipLaunchKernelGGL((attnbwd::attn_bwd_dq_kernel<D, DT, MASK, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((attnbwd::attn_bwd_dq_kernel<D, DT, MASK, NW, KG>), dim3((unsigned)grid), dim3(NW * KG * 64), 0,
+                       st, p);
     return hipGetLastError();
 }
 
@@ -588,7 +621,12 @@ hipError_t launch_main(const BwdParams &p, const Plan &pl, hipStream_t st) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    return pl.nw_q == 4 ? launch_dq<D, DT, MASK, 4>(p, pl.grid_q, st) : launch_dq<D, DT, MASK, 2>(p, pl.grid_q, st);
+    if constexpr (D == 64) {
+        if (pl.kg_q == 2)
+            return pl.nw_q == 4 ? launch_dq<D, DT, MASK, 4, 2>(p, pl.grid_q, st)
+                                : launch_dq<D, DT, MASK, 2, 2>(p, pl.grid_q, st);
+    }
+    return pl.nw_q == 4 ? launch_dq<D, DT, MASK, 4, 1>(p, pl.grid_q, st) : launch_dq<D, DT, MASK, 2, 1>(p, pl.grid_q, st);
 }
 
 template <int D, int DT>
@@ -607,6 +645,9 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int mas
     const bool masked = mask != attnfwd::MASK_NONE;
     pl.nw_kv = (masked && kv4 < kMinWorkgroups) ? 2 : 4;
     pl.nw_q = (masked && q4 < kMinWorkgroups) ? 2 : 4;
+    // d = 64 dQ on a grid of fewer than two 128-row workgroups per compute
+    // unit: two key groups per workgroup (twice the waves)
+    pl.kg_q = (d == 64 && q4 < kMinWorkgroups) ? 2 : 1;
     pl.grid_kv = B * Hkv * ((N + 32 * pl.nw_kv - 1) / (32 * pl.nw_kv)) * pl.hsplit;
     pl.grid_q = B * Hq * ((N + 32 * pl.nw_q - 1) / (32 * pl.nw_q));
     const int64_t rows_per_block = 256 / (d / 8);
