@@ -157,23 +157,30 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one workgroup per (batch, K/V head, BN = 32 * NW keys).
-// At d = 64 the register budget of two waves per SIMD is enough; asking for
-// it lets two workgroups share a compute unit.
-template <int D, int DT, int MASK, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+// dK and dV: one workgroup per (batch, K/V head, BN = 32 * NW keys).  With
+// QG = 2 a second set of NW waves owns the same keys and takes the second
+// half of the (head, query tile) steps with its own Q/dO ring; the two
+// partial dK, dV are summed in LDS at the end.  At d = 64 the register budget
+// of two waves per SIMD is enough; asking for it lets two workgroups share a
+// compute unit.
+template <int D, int DT, int MASK, int NW, int QG>
+__global__ __launch_bounds__(NW * QG * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
     constexpr int BN = 32 * NW;
     constexpr int BM = 64;                  // query rows per step
     constexpr int KT = D / 16;
     constexpr int CB = D / 32;
     constexpr int TILEB = BM * D * 2;
-    __shared__ __attribute__((aligned(1024))) char qs[2][TILEB];
-    __shared__ __attribute__((aligned(1024))) char dos[2][TILEB];
-    __shared__ __attribute__((aligned(16))) float2 dls[2][BM];
+    static_assert(QG == 1 || QG == 2, "one or two query groups");
+    static_assert(QG == 1 || NW * CB * 16 * 64 * 4 <= 2 * QG * TILEB, "Q ring too small for the dK/dV merge");
+    __shared__ __attribute__((aligned(1024))) char qs[2][QG * TILEB];
+    __shared__ __attribute__((aligned(1024))) char dos[2][QG * TILEB];
+    __shared__ __attribute__((aligned(16))) float2 dls[2][QG * BM];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wave_all % NW;         // keys of the wave
+    const int qg = wave_all / NW;           // its query group
     const int g = lane >> 5, l32 = lane & 31;
     const int N = p.N;
     const int bid = blockIdx.x;
@@ -214,29 +221,36 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     if constexpr (MASK == MASK_WINDOW) qt_end = min(qt_end, (j0 + BN - 1 + p.window - 1) / BM + 1);
     const int nq = max(qt_end - qt_begin, 0);
     const int nsteps = nq * gper;
+    // this query group's steps: [my_begin, my_begin + my_count); every wave
+    // runs `half` steps so that the workgroup barriers match
+    const int half = (nsteps + QG - 1) / QG;
+    const int my_begin = qg * half;
+    const int my_count = max(0, min(half, nsteps - qg * half));
 
     auto issue = [&](int s) {
-        const int h = hk * p.group + hs * gper + s / nq;
-        const int i0 = (qt_begin + s % nq) * BM;
+        const int st = my_begin + s;
+        const int h = hk * p.group + hs * gper + st / nq;
+        const int i0 = (qt_begin + st % nq) * BM;
         const int64_t bh = (int64_t)b * p.Hq + h;
-        load_rows<D, NW, BM>(p.q + bh * N * D, i0, N, qs[s & 1], wave, lane);
-        load_rows<D, NW, BM>(p.dout + bh * N * D, i0, N, dos[s & 1], wave, lane);
-        // D and L rows: 64 x 8 bytes by the 32 low lanes of wave 0 (rows
-        // padded to a multiple of 64, so always in bounds)
+        load_rows<D, NW, BM>(p.q + bh * N * D, i0, N, qs[s & 1] + qg * TILEB, wave, lane);
+        load_rows<D, NW, BM>(p.dout + bh * N * D, i0, N, dos[s & 1] + qg * TILEB, wave, lane);
+        // D and L rows: 64 x 8 bytes by the 32 low lanes of the group's wave 0
+        // (rows padded to a multiple of 64, so always in bounds)
         if (wave == 0 && lane < BM / 2)
             lds_dma16(p.dl + bh * p.Npad + i0 + 2 * lane,
-                      __builtin_amdgcn_readfirstlane(lds_addr(&dls[s & 1][0])));
+                      __builtin_amdgcn_readfirstlane(lds_addr(&dls[s & 1][qg * BM])));
     };
 
-    if (nsteps > 0) issue(0);
-    for (int s = 0; s < nsteps; ++s) {
+    if (my_count > 0) issue(0);
+    for (int s = 0; s < half; ++s) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         block_sync();
-        if (s + 1 < nsteps) issue(s + 1);
-        const int i0 = (qt_begin + s % nq) * BM;
-        const char *qt_l = qs[s & 1];
-        const char *dot_l = dos[s & 1];
-        const float2 *dl_l = dls[s & 1];
+        if (s + 1 < my_count) issue(s + 1);
+        if (s >= my_count) continue;
+        const int i0 = (qt_begin + (my_begin + s) % nq) * BM;
+        const char *qt_l = qs[s & 1] + qg * TILEB;
+        const char *dot_l = dos[s & 1] + qg * TILEB;
+        const float2 *dl_l = &dls[s & 1][qg * BM];
 #pragma unroll
         for (int qb = 0; qb < BM / 32; ++qb) {
             const int qa = i0 + 32 * qb;    // first query row of the block
@@ -302,6 +316,33 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
                     dka[cb] = mfma32<DT>(tr_frag<D>(qt_l, 2 * qb + ks, cb, lane), dsb[ks], dka[cb]);
                 }
         }
+    }
+
+    // query group 1 hands its partial dK^T and dV^T to group 0 through the
+    // idle Q and dO rings
+    if constexpr (QG == 2) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        float *bk = (float *)&qs[0][0];
+        float *bv = (float *)&dos[0][0];
+        if (qg == 1) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    bk[((wave * CB + cb) * 16 + r) * 64 + lane] = dka[cb][r];
+                    bv[((wave * CB + cb) * 16 + r) * 64 + lane] = dva[cb][r];
+                }
+        }
+        __syncthreads();
+        if (qg == 1) return;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dka[cb][r] += bk[((wave * CB + cb) * 16 + r) * 64 + lane];
+                dva[cb][r] += bv[((wave * CB + cb) * 16 + r) * 64 + lane];
+            }
     }
 
     // lane: key mykey, register r: channel 32 cb + 8 (r / 4) + 4 g + r % 4
@@ -589,14 +630,14 @@ int check_bwd_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, in
 // run on a small grid (lab N = 4096 causal: 0.257 -> 0.217 ms).  Unmasked
 // small grids stay at 4 (lab N = 4096: 0.232 ms at 4, 0.271 ms at 2).
 struct Plan {
-    int nw_kv, nw_q, kg_q, hsplit;
+    int nw_kv, nw_q, kg_q, qg_kv, hsplit;
     int64_t grid_kv, grid_q, grid_pre;
 };
 
-template <int D, int DT, int MASK, int NW>
+template <int D, int DT, int MASK, int NW, int QG>
 hipError_t launch_dkdv(const BwdParams &p, int64_t grid, hipStream_t st) {
-    hipLaunchKernelGGL((attnbwd::attn_bwd_dkdv_kernel<D, DT, MASK, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
-                       p);
+    hipLaunchKernelGGL((attnbwd::attn_bwd_dkdv_kernel<D, DT, MASK, NW, QG>), dim3((unsigned)grid), dim3(NW * QG * 64),
+                       0, st, p);
     return hipGetLastError();
 }
 
@@ -612,7 +653,17 @@ hipError_t launch_main(const BwdParams &p, const Plan &pl, hipStream_t st) {
     hipLaunchKernelGGL((attnbwd::attn_bwd_pre_kernel<D, DT>), dim3((unsigned)pl.grid_pre), dim3(256), 0, st, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = pl.nw_kv == 4 ? launch_dkdv<D, DT, MASK, 4>(p, pl.grid_kv, st) : launch_dkdv<D, DT, MASK, 2>(p, pl.grid_kv, st);
+    bool done = false;
+    if constexpr (D == 64) {
+        if (pl.qg_kv == 2) {
+            err = pl.nw_kv == 4 ? launch_dkdv<D, DT, MASK, 4, 2>(p, pl.grid_kv, st)
+                                : launch_dkdv<D, DT, MASK, 2, 2>(p, pl.grid_kv, st);
+            done = true;
+        }
+    }
+    if (!done)
+        err = pl.nw_kv == 4 ? launch_dkdv<D, DT, MASK, 4, 1>(p, pl.grid_kv, st)
+                            : launch_dkdv<D, DT, MASK, 2, 1>(p, pl.grid_kv, st);
     if (err != hipSuccess) return err;
     if (pl.hsplit > 1) {
         const int64_t n4 = (int64_t)p.n_bhk * p.N * D / 4;
@@ -648,6 +699,8 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int mas
     // d = 64 dQ on a grid of fewer than two 128-row workgroups per compute
     // unit: two key groups per workgroup (twice the waves)
     pl.kg_q = (d == 64 && q4 < kMinWorkgroups) ? 2 : 1;
+    // and two query groups per dK/dV workgroup likewise
+    pl.qg_kv = (d == 64 && kv4 < kMinWorkgroups) ? 2 : 1;
     pl.grid_kv = B * Hkv * ((N + 32 * pl.nw_kv - 1) / (32 * pl.nw_kv)) * pl.hsplit;
     pl.grid_q = B * Hq * ((N + 32 * pl.nw_q - 1) / (32 * pl.nw_q));
     const int64_t rows_per_block = 256 / (d / 8);
