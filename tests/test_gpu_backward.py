@@ -165,3 +165,40 @@ def test_bwd_lab_n4096_sampled(fa, causal):
 
 def test_bwd_gqa_n8192_sampled(fa):
     sampled_case(4, 32, 8, 8192, 128, "bf16", True, n_rows=32, n_keys=12)
+
+
+# ---- MQA long context at full size: the oracle cannot form every row's
+# normaliser for the per-key check here, so dq is checked on sampled rows and
+# dk, dv through identities that hold at any size (rows of P sum to 1, rows
+# of dS sum to 0): sum_j dv_j equals the sum of dO over every row of every
+# query head, and sum_j dk_j = 0, per channel.  The bound on each sum is 4 u
+# times the sum of the magnitudes it adds up (u as above).
+@pytest.mark.parametrize("window", [0, 4096])
+def test_bwd_mqa_n32768_properties(fa, window):
+    B, Hq, Hkv, N, d, dtype = 1, 32, 1, 32768, 128, "bf16"
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, dtype, seed=0)
+    do = make_dout(B, Hq, N, d, dtype, seed=0)
+    label = f"bwd MQA (1, 32/1, 32768, 128) bf16 causal W={window}"
+    say(f"case {label}")
+    dq, dk, dv = run_bwd(q, k, v, do, causal=True, window=window)
+    s = float(np.float32(1.0 / math.sqrt(d)))
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 4095, 4096, N - 1, 5 * N + 77], rng.integers(0, B * Hq * N, 24)]))
+    rq = oracle.oracle_bwd_rows(to_bits(q), to_bits(k), to_bits(v), to_bits(do), rows, scale=s, causal=True,
+                                window=window, dtype=dtype)
+    gq = dq.reshape(-1, d)[rows].to(torch.float64).numpy()
+    rel = float(np.abs(gq - rq).max() / np.abs(rq).max())
+    u = TOL_BWD[dtype] / 4
+    dvd = dv.to(torch.float64).numpy()[0, 0]
+    dkd = dk.to(torch.float64).numpy()[0, 0]
+    assert np.isfinite(dvd).all() and np.isfinite(dkd).all(), f"{label}: non-finite dk or dv"
+    want_dv = do.to(torch.float64).numpy().sum(axis=(0, 1, 2))
+    err_dv = np.abs(dvd.sum(0) - want_dv)
+    bound_dv = 4 * u * np.abs(dvd).sum(0)
+    err_dk = np.abs(dkd.sum(0))
+    bound_dk = 4 * u * np.abs(dkd).sum(0)
+    say(f"  {label}: dq rows {rel:.2e} x max|ref|; max |sum dv - sum dO| / bound {float((err_dv / bound_dv).max()):.2e}; "
+        f"max |sum dk| / bound {float((err_dk / bound_dk).max()):.2e}")
+    assert rel < TOL_BWD[dtype], f"{label}: dq error {rel:.2e} x max|ref|"
+    assert (err_dv < bound_dv).all(), f"{label}: sum of dv differs from the sum of dO"
+    assert (err_dk < bound_dk).all(), f"{label}: sum of dk is not 0"
