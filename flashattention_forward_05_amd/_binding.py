@@ -489,6 +489,8 @@ def flash_attn_backward(q, k, v, o, lse, dout, causal: bool = True, window: int 
             raise ValueError(f"{name} must be 4-D (B, H, N, d), got shape {tuple(t.shape)}")
     if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32:
         raise TypeError("lse must be the forward's float32 log-sum-exp tensor")
+    if any(t.device != q.device for t in (k, v, o, dout, lse)):
+        raise ValueError("q, k, v, o, dout and lse must be on one device")
     B, Hq, N, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)} disagree")

@@ -313,3 +313,11 @@ def test_bwd_rejects_before_touching_the_gpu():
         fa.attn_bwd(None, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A, 1, 1, 1, 8, 64, 0, 0, 0.1, 0,
                     10 * A, 1 << 16, 0)
     assert e.value.status == 1
+
+
+def test_flash_attn_backward_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    lse = torch.zeros(1, 2, 8, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        fa.flash_attn_backward(q, q, q, q, lse, q)
