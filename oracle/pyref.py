@@ -9,15 +9,20 @@ to things other than itself:
   "Bloque C", and the standard branch of the demo in "Optimizaciones de
   Atencion", section "FlashAttention: Nunca materializar la matriz de
   atencion".
-* ``online_attention`` -- the tiled online-softmax recurrence of that same demo
-  (Q blocks outer, K/V blocks inner, a running max and running sum per row,
-  previous partial results multiplied by exp(old_max - new_max), which is taken
-  as 0 while the old max is still -inf).  The page states that the tiled and
-  standard results agree to below 1e-10; the tests check this recurrence
-  against ``batch_attention`` and the C oracle.
+* ``online_attention`` -- the tiled computation that same demo checks: the
+  keys of a row are taken one block at a time, and what a block contributes
+  (its own max, its sum of exponentials against that max, its unnormalised
+  weighted sum of V rows) is folded into the row's result so far.  The fold
+  is the associative merge of two such triples, both re-based to the larger
+  max (``merge_partials``); that re-basing is the recurrence of the page's
+  running max and running sum, written here as a binary operator rather than
+  an in-place update.  The page states that the tiled and standard results
+  agree to below 1e-10; the tests check this against ``batch_attention`` and
+  the C oracle.
 * ``batch_softmax`` / ``online_softmax`` -- the one-vector identity behind the
   recurrence ("Fase 27 - Optimizaciones de atencion moderna", reading order,
-  lab 00: an online softmax in pure Python must equal the batch softmax).
+  lab 00: an online softmax in pure Python must equal the batch softmax),
+  the latter with the same merge on (max, sum) pairs.
 * ``split_kv_attention`` -- the three steps of "Optimizaciones de Atencion",
   section "FlashDecoding": cut the keys into P chunks of about s/P tokens, form
   per chunk a local softmax (local max m_p, local sum l_p) and the partial
@@ -57,18 +62,37 @@ def batch_softmax(xs):
     return [e / total for e in es]
 
 
+def merge_partials(a, b):
+    """Merge two partial softmax results (m, l, o) of disjoint key sets into the
+    result of their union: m is a max of scores, l the sum of exp(score - m)
+    and o (a list, possibly empty) the sum of exp(score - m) * value.  Both
+    sides are re-based to the larger max; an empty side has m = -inf and
+    contributes nothing.  The merge is associative and commutative."""
+    ma, la, oa = a
+    mb, lb, ob = b
+    if mb == NEG_INF:
+        return a
+    if ma == NEG_INF:
+        return b
+    m = max(ma, mb)
+    fa, fb = math.exp(ma - m), math.exp(mb - m)
+    return m, la * fa + lb * fb, [x * fa + y * fb for x, y in zip(oa, ob)]
+
+
+EMPTY = (NEG_INF, 0.0, [])
+
+
 def online_softmax(xs, block: int):
-    """Softmax of xs built block by block with a running max and running sum;
-    the exponentials are re-based to the final max at the end."""
-    run_max = NEG_INF
-    run_sum = 0.0
+    """Softmax of xs built from per-block (max, sum of exponentials) pairs,
+    folded left to right with ``merge_partials``; the exponentials are then
+    taken against the final max."""
+    state = EMPTY
     for start in range(0, len(xs), block):
         chunk = xs[start:start + block]
-        new_max = max(run_max, max(chunk))
-        corr = math.exp(run_max - new_max) if run_max != NEG_INF else 0.0
-        run_sum = run_sum * corr + math.fsum(math.exp(x - new_max) for x in chunk)
-        run_max = new_max
-    return [math.exp(x - run_max) / run_sum for x in xs]
+        mb = max(chunk)
+        state = merge_partials(state, (mb, math.fsum(math.exp(x - mb) for x in chunk), []))
+    m, total, _ = state
+    return [math.exp(x - m) / total for x in xs]
 
 
 def batch_attention(Q, K, V, scale: float, causal: bool = False, window: int = 0):
@@ -92,38 +116,40 @@ def batch_attention(Q, K, V, scale: float, causal: bool = False, window: int = 0
     return out, lse
 
 
+def _block_partial(q, K, V, js, scale: float):
+    """(m, l, o) of one query row over the keys js: the block's own max score,
+    its sum of exp(score - m) and its unnormalised weighted sum of V rows."""
+    d = len(V[0])
+    if not js:
+        return NEG_INF, 0.0, [0.0] * d
+    s = [scale * sum(a * b for a, b in zip(q, K[j])) for j in js]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    return m, math.fsum(w), [math.fsum(w[t] * V[j][c] for t, j in enumerate(js)) for c in range(d)]
+
+
 def online_attention(Q, K, V, scale: float, block_q: int, block_k: int,
                      causal: bool = False, window: int = 0):
-    """One head, tiled: Q blocks outer, K/V blocks inner, online softmax per
-    row.  Returns (O, LSE)."""
-    n, d = len(Q), len(V[0])
-    out = [[0.0] * d for _ in range(n)]
-    lse = [NEG_INF] * n
+    """One head, tiled: query rows in blocks of block_q, keys in blocks of
+    block_k.  Each row's result is the left fold of ``merge_partials`` over its
+    key blocks' partials, then o / l and m + ln l.  Returns (O, LSE)."""
+    n, nk, d = len(Q), len(K), len(V[0])
+    off = nk - n
+    key_blocks = [range(k0, min(k0 + block_k, nk)) for k0 in range(0, nk, block_k)]
+    out, lse = [], []
     for q0 in range(0, n, block_q):
-        rows = range(q0, min(q0 + block_q, n))
-        run_max = {i: NEG_INF for i in rows}
-        run_sum = {i: 0.0 for i in rows}
-        acc = {i: [0.0] * d for i in rows}
-        for k0 in range(0, len(K), block_k):
-            for i in rows:
-                js = [j for j in range(k0, min(k0 + block_k, len(K))) if visible(i, j, causal, window, len(K) - n)]
-                if not js:
-                    continue
-                scores = [scale * sum(a * b for a, b in zip(Q[i], K[j])) for j in js]
-                new_max = max(run_max[i], max(scores))
-                corr = math.exp(run_max[i] - new_max) if run_max[i] != NEG_INF else 0.0
-                run_sum[i] *= corr
-                acc[i] = [x * corr for x in acc[i]]
-                for t, j in enumerate(js):
-                    w = math.exp(scores[t] - new_max)
-                    run_sum[i] += w
-                    for c in range(d):
-                        acc[i][c] += w * V[j][c]
-                run_max[i] = new_max
-        for i in rows:
-            if run_sum[i] > 0.0:
-                out[i] = [x / run_sum[i] for x in acc[i]]
-                lse[i] = run_max[i] + math.log(run_sum[i])
+        for i in range(q0, min(q0 + block_q, n)):
+            state = (NEG_INF, 0.0, [0.0] * d)
+            for blk in key_blocks:
+                js = [j for j in blk if visible(i, j, causal, window, off)]
+                state = merge_partials(state, _block_partial(Q[i], K, V, js, scale))
+            m, total, o = state
+            if total > 0.0:
+                out.append([x / total for x in o])
+                lse.append(m + math.log(total))
+            else:
+                out.append([0.0] * d)
+                lse.append(NEG_INF)
     return out, lse
 
 
