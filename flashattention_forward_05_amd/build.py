@@ -11,21 +11,23 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattn_fwd.so")
-# (source, extra flags): the pipelined kernels keep MFMA results in VGPRs
+# the measured-ceilings kernels (microbench.py) are a library of their own
+MB_SOURCE = os.path.join(CSRC, "microbench.hip")
+MB_LIB_PATH = os.path.join(LIB_DIR, "libattn_microbench.so")
+# (source, extra flags)
 SOURCES = [
     (os.path.join(CSRC, "attn_fwd.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_d128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_paged64.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_paged128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_bwd.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
-    (os.path.join(CSRC, "attn_fwd_pipe.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Rpass-analysis=kernel-resource-usage"]),
+    (os.path.join(CSRC, "attn_fwd_pp.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
 ]
 # Kernels whose loads are tracked by explicit vmcnt waits must not touch
 # scratch memory (a spill reload would count as an outstanding load).
-NO_SCRATCH = ("attn_fwd_pipe_kernel", "attn_fwd_kernel", "attn_fwd_pingpong_kernel", "attn_bwd_dkdv_kernel",
-              "attn_bwd_dq_kernel")
-HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp", "attn_fwd_pingpong.hpp",
-                                            "attn_fwd_pipe.hpp", "attn_fwd_launch.hpp",
+NO_SCRATCH = ("attn_fwd_kernel", "attn_fwd_pp_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel")
+HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp", "attn_fwd_pp.hpp",
+                                            "attn_fwd_launch.hpp",
                                             "attn_fwd_merge.hpp", "attn_fwd_lockstep.hpp")] + [
     os.path.join(INCLUDE, "attn_fwd.h"), os.path.join(INCLUDE, "attn_bwd.h")]
 
@@ -66,9 +68,12 @@ def _run(cmd: list[str], verbose: bool) -> None:
 
 
 def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = None) -> str:
-    """Compile every source (always, in parallel) and atomically replace the library."""
+    """Compile every source (always, in parallel) and atomically replace the
+    library; also builds the microbenchmark library next to it."""
     os.makedirs(os.path.dirname(out), exist_ok=True)
     objs, procs = [], []
+    mb_tmp = MB_LIB_PATH + ".tmp"
+    mb_cmd = [HIPCC, *FLAGS, "-shared", MB_SOURCE, "-o", mb_tmp]
     for src, flags in SOURCES:
         obj = os.path.join(os.path.dirname(out), os.path.basename(src) + ".o")
         cmd = [HIPCC, *FLAGS, *flags, *(extra or []), "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
@@ -76,8 +81,9 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra: list[str] | None = 
         procs.append(cmd)
     # the translation units are independent: compile them concurrently
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(len(procs)) as ex:
-        list(ex.map(lambda c: _run(c, verbose), procs))
+    with ThreadPoolExecutor(len(procs) + 1) as ex:
+        list(ex.map(lambda c: _run(c, verbose), procs + [mb_cmd]))
+    os.replace(mb_tmp, MB_LIB_PATH)
     tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     for o in objs:

@@ -12,7 +12,6 @@
 #include "attn_fwd_launch.hpp"
 #include "attn_fwd_lockstep.hpp"
 #include "attn_fwd_merge.hpp"
-#include "attn_fwd_pingpong.hpp"
 
 namespace {
 
@@ -21,46 +20,42 @@ using attnfwd::Params;
 // Tile configurations compiled into the library.  qb: 32-row query blocks
 // per wave; nwq: query waves per workgroup; ksplit: key groups per workgroup
 // (2 or 4 = further sets of waves take later parts of the key range, merged
-// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring (of
-// each of the K and V rings for kind 2); kind: 0 = lockstep kernel, 1 =
-// ping-pong (the two wave groups alternate matrix and vector phases; then
-// ksplit = 1 means the groups own different query rows), 2 = in-wave
-// pipelined kernel.  The same id may use a smaller tile for d = 128 so that
-// LDS and registers fit.
+// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring; kind: 0
+// = lockstep kernel (attn_fwd_kernel.hpp), 1 = ping-pong kernel
+// (attn_fwd_pp.hpp: two groups of four waves own 128 rows each and alternate
+// matrix and vector phases).  The same id may use a smaller tile for d = 128
+// so that LDS and registers fit.
 struct TileCfg {
     int qb, nwq, ksplit, bn, nstage, kind;
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 10;
+constexpr int kNumConfigs = 8;
+constexpr int kPingPong = 4;
 constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
     {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
     {1, 8, 1, 64, 3, 0},   // 2: 256 rows, 8 waves
     {2, 4, 1, 64, 3, 0},   // 3: 256 rows, 4 waves with 64 rows each
-    {1, 8, 1, 64, 4, 1},   // 4: ping-pong, 256 rows in two row groups
-    {1, 4, 2, 64, 4, 1},   // 5: ping-pong, 128 rows, two key groups
-    {1, 4, 1, 64, 3, 2},   // 6: pipelined, 128 rows, 4 waves
-    {1, 2, 2, 64, 2, 0},   // 7: 64 rows, 4 waves (two key groups), two workgroups per CU
-    {1, 1, 1, 64, 3, 0},   // 8: 32 rows, 1 wave (few query rows: decoding)
-    {1, 1, 4, 64, 2, 0},   // 9: 32 rows, 4 waves in four key groups (small grids)
+    {1, 8, 1, 64, 4, 1},   // 4: ping-pong, 256 rows in two groups of four waves
+    {1, 2, 2, 64, 2, 0},   // 5: 64 rows, 4 waves (two key groups), two workgroups per CU
+    {1, 1, 1, 64, 3, 0},   // 6: 32 rows, 1 wave (few query rows: decoding)
+    {1, 1, 4, 64, 2, 0},   // 7: 32 rows, 4 waves in four key groups (small grids)
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 1, 64, 3, 0},
     {1, 4, 2, 64, 2, 0},
     {1, 8, 1, 64, 3, 0},
     {2, 4, 1, 32, 3, 0},
-    {1, 8, 1, 32, 4, 1},
-    {1, 4, 2, 32, 4, 1},
-    {1, 4, 1, 32, 3, 2},
+    {1, 8, 1, 64, 4, 1},
     {1, 2, 2, 32, 2, 0},
     {1, 1, 1, 32, 3, 0},
     {1, 1, 4, 32, 2, 0},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
-// Configurations not built for a head dim (the ping-pong kernel at d = 128).
-bool cfg_built(int64_t d, int id) { return !(d == 128 && tile_cfg(d, id).kind == 1); }
+// Every configuration is built for both head dims.
+bool cfg_built(int64_t, int) { return true; }
 
 // Query tiles whose first row sees fewer keys than this use the two-term P.
 constexpr int kExactBelow = 256;
@@ -91,53 +86,23 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int ca
 }
 
 // Automatic choice (measured on MI355X).  d = 128 with at least two 256-row
-// workgroups per compute unit runs 8 query waves of 32 rows (2); other
-// d = 128 shapes run 128-row workgroups with two key groups (1).  For d = 64,
-// 64-row workgroups, two per compute unit (7), win on small grids and on
-// masked runs, where they spread the uneven causal work over twice as many
+// workgroups per compute unit runs 8 query waves of 32 rows (2); smaller
+// d = 128 grids run 128-row workgroups with two key groups (1).  The
+// ping-pong kernel (4) measured slower than 2 on every prefill workload.  For d = 64, 64-row
+// workgroups, two per compute unit (5), win on small grids and on masked
+// runs, where they spread the uneven causal work over twice as many
 // workgroups; larger unmasked grids keep the 128-row workgroups (1).  When
 // even 32-row workgroups are at most one per compute unit, 32 rows with four
-// key groups (9) keep every SIMD busy (lab N = 1024: 183 -> 231 TFLOP/s
-// unmasked, 88 -> 112 causal).
+// key groups (7) keep every SIMD busy.
 int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask) {
     const int64_t wg128 = B * Hq * ((N + 127) / 128);
     if (d == 128) {
         const int64_t wg256 = B * Hq * ((N + 255) / 256);
         return wg256 >= 512 ? 2 : 1;
     }
-    if (B * Hq * ((N + 31) / 32) <= 256) return 9;
-    if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 7 : 1;
-    return wg128 < 128 ? 7 : 1;
-}
-
-template <int D, int DT, int MASK, int NWG, bool ROWS, int BN>
-hipError_t launch_pp(const Params &p, int64_t grid, hipStream_t stream) {
-    Params args = p;
-    void *argv[] = {&args};
-    return hipLaunchKernel((const void *)&attnfwd::attn_fwd_pingpong_kernel<D, DT, MASK, NWG, ROWS, BN>,
-                           dim3((unsigned)grid), dim3(2 * NWG * 64), argv, 0, stream);
-}
-
-// d = 64, contiguous K/V: lockstep configurations here, ping-pong (4, 5; built
-// for d = 64 only: at d = 128 it does not fit its registers without
-// spilling) and pipelined (6, its own translation unit).
-template <int DT, int MASK>
-hipError_t launch_cfg64(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
-    switch (cfg) {
-    case 4: return launch_pp<64, DT, MASK, 4, true, 64>(p, grid, stream);
-    case 5: return launch_pp<64, DT, MASK, 4, false, 64>(p, grid, stream);
-    case 6: return attnfwd::launch_pipelined(64, DT, MASK, cfg, p, grid, stream);
-    default: return attnfwd::launch_lockstep_cfg<64, DT, MASK, false>(cfg, p, grid, stream);
-    }
-}
-
-template <int DT>
-hipError_t launch_mask64(int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream) {
-    switch (mask) {
-    case attnfwd::MASK_NONE: return launch_cfg64<DT, attnfwd::MASK_NONE>(cfg, p, grid, stream);
-    case attnfwd::MASK_CAUSAL: return launch_cfg64<DT, attnfwd::MASK_CAUSAL>(cfg, p, grid, stream);
-    default: return launch_cfg64<DT, attnfwd::MASK_WINDOW>(cfg, p, grid, stream);
-    }
+    if (B * Hq * ((N + 31) / 32) <= 256) return 7;
+    if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 5 : 1;
+    return wg128 < 128 ? 5 : 1;
 }
 
 // Routes a launch to the translation unit that holds its instantiation.
@@ -147,9 +112,8 @@ hipError_t launch(int64_t d, int dtype, int mask, int cfg, const Params &p, int6
     if (p.paged)
         return d == 64 ? attnfwd::launch_lockstep_paged64(dt, mask, cfg, p, grid, stream)
                        : attnfwd::launch_lockstep_paged128(dt, mask, cfg, p, grid, stream);
-    if (d == 64)
-        return dt == 0 ? launch_mask64<0>(mask, cfg, p, grid, stream) : launch_mask64<1>(mask, cfg, p, grid, stream);
-    if (cfg == 6) return attnfwd::launch_pipelined(128, dt, mask, cfg, p, grid, stream);
+    if (cfg == kPingPong) return attnfwd::launch_pingpong(d, dt, mask, p, grid, stream);
+    if (d == 64) return attnfwd::launch_lockstep_d64(dt, mask, cfg, p, grid, stream);
     return attnfwd::launch_lockstep_d128(dt, mask, cfg, p, grid, stream);
 }
 
@@ -276,10 +240,11 @@ KvView kv_view(int64_t Hq, int64_t Hkv, int64_t Nq) {
 // of the plain forward, with 64-row workgroups (7) in place of the four-key-
 // group ones (9): key chunks already spread a small grid.
 int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask) {
-    if (Nq < 32) return 8;
+    if (Nq < 32) return 6;
     if (Nq <= 128) return 1;
     const int id = auto_config(B, Hq, Nq, d, mask);
-    return id == 9 ? 7 : id;
+    if (id == 7) return 5;
+    return id == kPingPong ? 2 : id;
 }
 
 struct SplitPlan {
@@ -317,6 +282,14 @@ SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t q_fi
 }
 
 }  // namespace
+
+namespace attnfwd {
+
+hipError_t launch_lockstep_d64(int dt, int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream) {
+    return launch_lockstep_d<64, false>(dt, mask, cfg, p, grid, stream);
+}
+
+}  // namespace attnfwd
 
 extern "C" {
 
@@ -421,24 +394,25 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     const int mask = mask_mode(causal, window);
     Params p = make_params(q, k, v, o, lse, B, Hq, Hkv, N, N, window, mask, scale, ntiles);
     // two 64-row workgroups share a compute unit: pair heavy and light tiles
-    p.zigzag = (id == 7) ? 1 : 0;
+    p.zigzag = (id == 5) ? 1 : 0;
 
     hipError_t err = hipSuccess;
-    if (tc.kind == 2) {
-        // The pipelined kernel has no two-term-P path: the leading query
+    if (tc.kind == 1) {
+        // The ping-pong kernel has no two-term-P path: the leading query
         // tiles whose first row sees few keys (a prefix in tile order) run on
-        // the lockstep kernel with the same 128-row tiling, the rest on the
-        // pipelined one (it takes the tiles from the last down, so n_qtiles
-        // keeps its meaning there).  The two launches write disjoint rows.
+        // the lockstep kernel with the same 256-row tiling (configuration 2),
+        // the rest on the ping-pong kernel, which takes its tiles from the
+        // last down, so n_qtiles keeps its meaning there.  Unmasked calls
+        // have such tiles only when N is below the threshold, and then every
+        // tile is one.  The two launches write disjoint rows.
         const int64_t n_exact = exact_tiles(N, causal, mask == attnfwd::MASK_WINDOW ? p.window : 0, bm);
-        if (n_exact > 0) {
+        const int64_t n_pp = (mask == attnfwd::MASK_NONE && n_exact > 0) ? 0 : ntiles - n_exact;
+        if (n_pp < ntiles) {
             Params pe = p;
-            pe.n_qtiles = (int)n_exact;
-            pe.zigzag = 0;
-            err = launch(d, dtype, mask, 0, pe, B * Hq * n_exact, (hipStream_t)stream);
+            pe.n_qtiles = (int)(ntiles - n_pp);
+            err = launch(d, dtype, mask, 2, pe, B * Hq * (ntiles - n_pp), (hipStream_t)stream);
         }
-        if (err == hipSuccess && n_exact < ntiles)
-            err = launch(d, dtype, mask, id, p, B * Hq * (ntiles - n_exact), (hipStream_t)stream);
+        if (err == hipSuccess && n_pp > 0) err = launch(d, dtype, mask, id, p, B * Hq * n_pp, (hipStream_t)stream);
     } else {
         err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
     }
@@ -544,7 +518,7 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
                            scale, sp.ntiles);
     p.q_off = (int)(Nk - Nq);
     p.pack_nq = kv.pack_nq;
-    p.zigzag = (id == 7) ? 1 : 0;
+    p.zigzag = (id == 5) ? 1 : 0;
     p.n_splits = (int)sp.n_splits;
     p.split_tiles = (int)sp.split_tiles;
     p.split_t0 = (int)sp.t0;
@@ -725,7 +699,7 @@ int attn_fwd_paged_ex(const void *q, const void *k_pool, const void *v_pool, con
                            window, mask, scale, sp.ntiles);
     p.q_off = (int)(max_seq_len - Nq);   // replaced per batch from seq_lens in the kernel
     p.pack_nq = kv.pack_nq;
-    p.zigzag = (id == 7) ? 1 : 0;
+    p.zigzag = (id == 5) ? 1 : 0;
     p.n_splits = (int)sp.n_splits;
     p.split_tiles = (int)sp.split_tiles;
     p.split_t0 = 0;

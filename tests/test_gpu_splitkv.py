@@ -15,7 +15,7 @@ from gpu_helpers import (TOL_LSE, TOL_O, check, need_gpu, oracle_full, oracle_sa
 
 pytestmark = pytest.mark.gpu
 
-LOCKSTEP_CONFIGS = (0, 1, 2, 3, 7, 8)
+LOCKSTEP_CONFIGS = (0, 1, 2, 3, 5, 6)
 
 
 @pytest.fixture(scope="module")
@@ -64,7 +64,7 @@ def test_splitkv_all_configs_and_chunk_counts(fa, case):
 
 def test_splitkv_other_kernels_rejected(fa):
     q, k, v = qkv(1, 2, 2, 1, 100, 64, "f16", seed=1)
-    for cfg in (4, 5, 6):
+    for cfg in (4,):
         with pytest.raises(fa.AttnError) as e:
             run_gpu_splitkv(q, k, v, causal=True, config_id=cfg)
         assert e.value.status == 3
@@ -165,7 +165,7 @@ def test_splitkv_random_shapes(fa):
         causal = bool(rng.integers(0, 4) > 0)
         window = int(rng.choice([0, 0, 1, 7, 300])) if causal else 0
         splits = int(rng.choice([0, 1, 2, 5, 64]))
-        cfg = int(rng.choice([-1, 0, 1, 7, 8]))
+        cfg = int(rng.choice([-1, 0, 1, 5, 6]))
         q, k, v = qkv(B, G * Hkv, Hkv, Nq, Nk, d, dt, seed=100 + n)
         ro, rl = oracle_full(q, k, v, causal=causal, window=window)
         o, lse = run_gpu_splitkv(q, k, v, causal=causal, window=window, num_splits=splits, config_id=cfg)
