@@ -3,9 +3,9 @@
 
 A step runs the whole hot path over one batch of synthetic input: every
 (N, causal) variant of the workload, each one launch of the fused kernel
-through the C ABI.  Default workload: the pages' lab check (B=2, Hq=Hkv=4,
-d=64, fp16, N in {256, 1024, 4096}, causal and not; "Lab 02 - Forward de flash
-attention en Triton", "Bloque D").
+through the C ABI.  The pages' lab check (B=2, Hq=Hkv=4, d=64, fp16, N in
+{256, 1024, 4096}, causal and not; "Lab 02 - Forward de flash attention en
+Triton", "Bloque D") is --workload lab.
 
 Metric: attention-forward TFLOP/s with 4*B*Hq*N^2*d FLOPs per variant, halved
 when causal; a sliding window counts its visible (query, key) pairs instead.
@@ -18,9 +18,15 @@ with a workspace allocated before timing; ``--splitkv`` runs any workload that
 way.  Their FLOPs are 4*d per visible (query, key) pair, and since they move
 far more bytes than they compute on, their roofline is HBM bandwidth.
 
+Default workload: the largest single-GPU configuration, MQA long context
+(B=1, Hq=32, Hkv=1, N=32768, d=128, bf16), causal with a 4096-token sliding
+window and full causal; a step runs both.  The lab check (d=64, fp16) and the
+other workloads are selectable with --workload.
+
 Prints one JSON line.  Extra fields: "roofline" for the dominant kernel
 (achieved = its FLOPs, or algorithmic bytes, per launch / its mean launch time
-from HIP events on the launch stream) and "cpu_baseline" (the fp64 oracle on a
+from HIP events on the launch stream; beside the published peak, the MFMA rate
+measured on this GPU by microbench.py) and "cpu_baseline" (the fp64 oracle on a
 bounded sample of the same workload, on this host's cores).
 """
 from __future__ import annotations
@@ -64,6 +70,21 @@ def metric_flops(B, Hq, N, d, causal, window=0) -> float:
         return 4.0 * B * Hq * d * pairs
     f = 4.0 * B * Hq * N * N * d
     return f / 2 if causal else f
+
+
+def page_naive_score_bytes(N, elem=4) -> float:
+    """HBM bytes the unfused attention moves for the N x N score matrix of one
+    head: S written, read back for the softmax, P written, read back for
+    P.V ("00 - Por que la atencion domina la inferencia", section "Por que la
+    attention es bandwidth-bound": 16 N^2 bytes in fp32)."""
+    return 4.0 * elem * N * N
+
+
+def page_tiled_bytes(N, d, block, elem=4) -> float:
+    """The same page's model of the tiled kernel's traffic for one head,
+    N d (3 + 2 N / block) elements (section "Lo que Flash hace de verdad, en
+    un parrafo"): K and V read once per query block of `block` rows."""
+    return float(N) * d * (3.0 + 2.0 * N / block) * elem
 
 
 def visible_keys(i, N, causal, window, Nk=None):
@@ -280,10 +301,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="lab", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--workload", default="mqa", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--config", type=int, default=-1, help="tile configuration id (-1: automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-microbench", action="store_true",
+                    help="skip the measured MFMA peak (microbench.py) reported beside the published one")
     ap.add_argument("--splitkv", action="store_true",
                     help="run every variant through the split-KV entry point (decoding workloads always are)")
     ap.add_argument("--splits", type=int, default=0, help="key chunks for split-KV calls (0: automatic)")
@@ -474,6 +497,14 @@ def main() -> int:
         per_kernel_ms.append(a.elapsed_time(b) / reps)
         del g
 
+    # the MFMA rate this GPU reaches on a pure 32x32x16 bf16 loop (after the
+    # timed region, so it does not heat the GPU before it)
+    measured = None
+    if not args.no_microbench:
+        from flashattention_forward_05_amd import microbench
+        mb = microbench.measure(quick=True)
+        measured = {"tflops": round(mb["mfma_32x32x16_bf16_tflops"], 1), "clock_ghz": round(mb["clock_ghz_mfma"], 3)}
+
     total_flops = sum(r["flops"] for r in runs)
     ms_per_step = wall * 1e3 / args.steps
     value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -533,6 +564,17 @@ def main() -> int:
             "frac": round(roof["achieved"] / roof["peak"], 4),
             "traffic": traffic_from_profiles(label(runs[dom]), "bwd" if args.backward else "fwd"),
             **({"algorithmic_bytes": roof["algorithmic_bytes"]} if "algorithmic_bytes" in roof else {}),
+            "algorithmic_intensity": round(runs[dom]["flops"] / runs[dom]["bytes"], 1),
+            # the pages' byte models at this shape (16-bit elements, per head
+            # times B * Hq): the unfused score-matrix traffic, and the tiled
+            # kernel's with K/V read once per query tile of the plan's rows
+            "page_naive_score_bytes": page_naive_score_bytes(dw.N, 2) * dw.B * dw.Hq,
+            "page_tiled_model_bytes": page_tiled_bytes(dw.N, dw.d, runs[dom]["plan"].get("block_m", 64), 2)
+            * dw.B * dw.Hq,
+            "ridge": round(RIDGE, 1),
+            **({"measured_peak": measured["tflops"], "frac_of_measured_peak":
+                round(roof["achieved"] / measured["tflops"], 4), "measured_clock_ghz": measured["clock_ghz"]}
+               if measured and roof["bound"] == "mfma" else {}),
         },
         "kernels": kernels,
         "frac_of_peak_whole_step": round(value / PEAK_TFLOPS[wls[0].dtype], 4),
