@@ -196,6 +196,27 @@ def tuned_configs() -> dict:
     return dict(_TUNED)
 
 
+def _check_buffer(name, t, device, dtype=None, shape=None):
+    """Reject a caller-supplied tensor the kernels would misuse before any GPU
+    work: it must be a tensor on `device` (TypeError for a host tensor or a
+    wrong dtype, ValueError for another GPU, a wrong shape or a
+    non-contiguous layout: the kernels write it densely by raw pointer)."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != device.type:
+        raise TypeError(f"{name} must be on {device.type}, got {t.device}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None,
                        config_id: int = -1, out=None, lse=None, return_lse: bool = True, tune: bool = False):
     """(B, Hq, N, d) query, (B, Hkv, N, d) key/value fp16 or bf16 CUDA tensors
@@ -219,14 +240,19 @@ def flash_attn_forward(q, k, v, causal: bool = True, window: int = 0, scale: flo
     B, Hq, N, d = q.shape
     if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     Hkv = k.shape[1]
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("out", out, q.device, q.dtype, q.shape)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (B, Hq, N))
     dtype = ATTN_F16 if q.dtype == torch.float16 else ATTN_BF16
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -314,6 +340,8 @@ def flash_attn_forward_splitkv(q, k, v, causal: bool = True, window: int = 0, sc
     B, Hq, Nq, d = q.shape
     if k.shape[0] != B or k.shape[3] != d:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     Hkv, Nk = k.shape[1], k.shape[2]
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     if scale is None:
@@ -322,11 +350,16 @@ def flash_attn_forward_splitkv(q, k, v, causal: bool = True, window: int = 0, sc
     need = attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits, config_id)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("out", out, q.device, q.dtype, q.shape)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (B, Hq, Nq))
     with torch.cuda.device(q.device):
         attn_fwd_splitkv_ex(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
                             num_splits, config_id, workspace, ws_bytes,
@@ -422,6 +455,8 @@ def flash_attn_forward_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_l
     num_pages, Hkv, page_size, dk = k_pool.shape
     if dk != d or block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("inconsistent paged shapes")
+    if any(t.device != q.device for t in (k_pool, v_pool, block_table, seq_lens)):
+        raise ValueError("q, the pools, block_table and seq_lens must be on one device")
     max_pages = block_table.shape[1]
     if max_seq_len is None:
         max_seq_len = max_pages * page_size
@@ -434,11 +469,16 @@ def flash_attn_forward_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_l
                                          window, dtype, num_splits, config_id)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("out", out, q.device, q.dtype, q.shape)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (B, Hq, Nq))
     with torch.cuda.device(q.device):
         attn_fwd_paged_ex(q, k_pool, v_pool, block_table, seq_lens, out, lse, B, Hq, Hkv, Nq, d, page_size,
                           num_pages, max_pages, max_seq_len, causal, window, scale, dtype, num_splits, config_id,
