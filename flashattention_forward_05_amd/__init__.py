@@ -17,7 +17,9 @@ Split-KV ("Optimizaciones de Atencion", section "FlashDecoding"):
 ``attn_fwd_splitkv``, ``attn_fwd_splitkv_ex``, ``attn_fwd_splitkv_validate``,
 ``attn_fwd_splitkv_plan``, ``attn_fwd_splitkv_workspace_size`` and the
 convenience ``flash_attn_forward_splitkv(q, k, v, causal=True)`` for Nq
-queries against Nk keys (decoding).
+queries against Nk keys (decoding); ``attn_fwd_splitkv_noalloc`` is the same
+call with its partials in a fixed per-device array of the library, for
+callers that cannot allocate.
 
 Paged K/V ("00 - Por que la atencion domina la inferencia", section
 "PagedAttention es un problema distinto"): ``attn_fwd_paged``,
@@ -32,6 +34,7 @@ the scores recomputed tile by tile.
 from ._binding import (  # noqa: F401
     ATTN_BF16,
     ATTN_F16,
+    ATTN_NOALLOC_SCRATCH_BYTES,
     STATUS,
     AttnError,
     attn_bwd,
@@ -51,6 +54,7 @@ from ._binding import (  # noqa: F401
     attn_fwd_plan_ex,
     attn_fwd_splitkv,
     attn_fwd_splitkv_ex,
+    attn_fwd_splitkv_noalloc,
     attn_fwd_splitkv_plan,
     attn_fwd_splitkv_validate,
     attn_fwd_splitkv_workspace_size,

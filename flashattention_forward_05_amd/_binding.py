@@ -13,8 +13,9 @@ ATTN_BF16 = 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_ARG", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_LAUNCH",
-    8: "ATTN_ERR_DEVICE", 9: "ATTN_ERR_WORKSPACE",
+    8: "ATTN_ERR_DEVICE", 9: "ATTN_ERR_WORKSPACE", 10: "ATTN_ERR_SCRATCH",
 }
+ATTN_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _lib = None
 
@@ -64,6 +65,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_splitkv.restype = cint
     lib.attn_fwd_splitkv_ex.argtypes = kv + [cint, vp, i64, vp]
     lib.attn_fwd_splitkv_ex.restype = cint
+    lib.attn_fwd_splitkv_noalloc.argtypes = kv + [cint, vp]
+    lib.attn_fwd_splitkv_noalloc.restype = cint
     lib.attn_fwd_splitkv_validate.argtypes = kv + [cint, vp, i64]
     lib.attn_fwd_splitkv_validate.restype = cint
     lib.attn_fwd_splitkv_plan.argtypes = [i64, i64, i64, i64, i64, i64, cint, i64, cint, i64, cint, i64p]
@@ -305,6 +308,17 @@ def attn_fwd_splitkv_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, 
         dtype, num_splits, config_id, _ptr(workspace), workspace_bytes, _stream(stream))
     if rc != 0:
         raise AttnError(rc, "attn_fwd_splitkv_ex")
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,
+                             num_splits=0, config_id=-1, stream=None) -> None:
+    """Enqueue the split-KV forward with its partials in the library's fixed
+    per-device scratch (no allocation); raises AttnError."""
+    rc = load_library().attn_fwd_splitkv_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal), window, scale,
+        dtype, num_splits, config_id, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_splitkv_noalloc")
 
 
 def attn_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype,

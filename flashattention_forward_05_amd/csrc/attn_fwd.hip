@@ -3,10 +3,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn_fwd.h"
 #include "attn_fwd_launch.hpp"
@@ -305,6 +307,7 @@ const char *attn_status_str(int status) {
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_DEVICE: return "no usable gfx950 device";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_fwd_splitkv_workspace_size";
+    case ATTN_ERR_SCRATCH: return "split-KV partials larger than the fixed scratch of attn_fwd_splitkv_noalloc";
     default: return "unknown status";
     }
 }
@@ -539,6 +542,68 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
         err = launch_merge(d, dtype, mp, (hipStream_t)stream);
     }
     return status_of(err);
+}
+
+}  // extern "C"
+
+// ---- split-KV without allocation -----------------------------------------
+// attn_fwd_splitkv_noalloc keeps its chunk partials in this fixed array
+// instead of a caller workspace.  Each device holds its own copy from module
+// load to process exit.  Host code must never pass `scratch` itself to a
+// kernel: on the host the name is a stand-in, not the device address, which
+// is looked up once per device with hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device (with it current) and kept.
+int scratch_ptr(void **out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return status_of(err);
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (err != hipSuccess || !p) return err != hipSuccess ? status_of(err) : ATTN_ERR_DEVICE;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                             int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                             int64_t window, float scale, int dtype, int64_t num_splits, int config_id,
+                             void *stream) {
+    // every host check that needs no device first, so an oversized call fails
+    // before any HIP call
+    int64_t plan[9];
+    int rc = attn_fwd_splitkv_plan(B, Hq, Hkv, Nq, Nk, d, causal, window, dtype, num_splits, config_id, plan);
+    if (rc != ATTN_OK) return rc;
+    if (plan[7] > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    if (Nq == 0) return attn_fwd_splitkv_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale,
+                                                  dtype, num_splits, config_id, nullptr, 0);
+    void *ws = nullptr;
+    if (plan[7] > 0) {
+        rc = scratch_ptr(&ws);
+        if (rc != ATTN_OK) return rc;
+    }
+    return attn_fwd_splitkv_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, dtype, num_splits,
+                               config_id, ws, ws ? ATTN_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 // ---- tile-configuration tuning ------------------------------------------

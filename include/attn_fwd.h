@@ -75,7 +75,8 @@ typedef enum {
     ATTN_ERR_ALIAS = 6,       /* o or lse overlaps q, k, v or each other */
     ATTN_ERR_LAUNCH = 7,      /* the kernel launch itself failed */
     ATTN_ERR_DEVICE = 8,      /* no usable gfx950 device is current */
-    ATTN_ERR_WORKSPACE = 9    /* split-KV workspace smaller than attn_fwd_splitkv_workspace_size */
+    ATTN_ERR_WORKSPACE = 9,   /* split-KV workspace smaller than attn_fwd_splitkv_workspace_size */
+    ATTN_ERR_SCRATCH = 10     /* attn_fwd_splitkv_noalloc: partials exceed ATTN_NOALLOC_SCRATCH_BYTES */
 } attn_status_t;
 
 /*
@@ -235,6 +236,28 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                         int causal, int64_t window, float scale, int dtype, int64_t num_splits,
                         int config_id, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_splitkv_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The chunk partials go to a fixed array of
+ * ATTN_NOALLOC_SCRATCH_BYTES inside the library (one per device, alive until
+ * the process ends) instead of a caller workspace; the caller still owns q, k,
+ * v, o and lse.  The call allocates and frees nothing.  The first call on a
+ * device looks the array's address up once (hipGetSymbolAddress, with that
+ * device current).  Every call on a device shares its array, so calls on one
+ * device that may overlap in time (distinct streams without ordering) race
+ * and give wrong results; nothing in the array needs clearing between calls.
+ * Arguments, layout, results and errors: those of attn_fwd_splitkv_ex, plus
+ * ATTN_ERR_SCRATCH (nothing launched) when the partials of the chosen split,
+ * attn_fwd_splitkv_workspace_size(...) bytes, exceed the array; a smaller
+ * num_splits then fits.  That check is made on the host before any HIP call.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                             int causal, int64_t window, float scale, int dtype, int64_t num_splits,
+                             int config_id, void *stream);
 
 /* Bytes of workspace a split-KV call with these arguments needs (0 when it
  * uses one chunk), or minus the status code when the sizes are invalid.  Pure

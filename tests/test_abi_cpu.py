@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         assert fa.attn_status_str(code) and fa.attn_status_str(code) != "unknown status"
     assert fa.attn_status_str(99) == "unknown status"
 
@@ -345,3 +345,22 @@ def test_flash_attn_forward_rejects_host_tensors():
     for fn in (fa.flash_attn_forward, fa.flash_attn_forward_splitkv):
         with pytest.raises(TypeError):
             fn(q, q, q)
+
+
+def test_noalloc_rejects_oversized_partials_on_host():
+    """attn_fwd_splitkv_noalloc refuses a split whose partials exceed its fixed
+    scratch, and does so before any HIP call (this runs with no GPU)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 16, 16, 512, 4096, 128
+    need = fa.attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, True, 0, fa.ATTN_BF16, 64, -1)
+    assert need > fa.ATTN_NOALLOC_SCRATCH_BYTES
+    base = 1 << 40
+    q, k, v, o = base, base + (1 << 30), base + (2 << 30), base + (3 << 30)
+    with pytest.raises(fa.AttnError) as e:
+        fa.attn_fwd_splitkv_noalloc(q, k, v, o, None, B, Hq, Hkv, Nq, Nk, d, True, 0, 0.1, fa.ATTN_BF16, 64, -1,
+                                    stream=0)
+    assert e.value.status == 10
+    # sizes the plain split-KV entry point rejects are rejected the same way
+    with pytest.raises(fa.AttnError) as e:
+        fa.attn_fwd_splitkv_noalloc(q, k, v, o, None, B, Hq, 5, Nq, Nk, d, True, 0, 0.1, fa.ATTN_BF16, 64, -1,
+                                    stream=0)
+    assert e.value.status == 2
