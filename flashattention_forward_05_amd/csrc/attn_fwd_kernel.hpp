@@ -31,9 +31,10 @@
 //    is the V^T A-operand layout (8 consecutive keys of one channel per lane).
 //  * K and V tiles are brought to LDS by direct global->LDS loads
 //    (global_load_lds_dwordx4) into an NSTAGE-deep ring: tiles i+1 ..
-//    i+NSTAGE-2 are in flight while tile i is used.  Each ring stage is its
-//    own LDS object and the loop is unrolled over the stages, so the compiler
-//    can tell that reads of one stage do not alias loads into another; the
+//    i+NSTAGE-2 are in flight while tile i is used.  The loop is unrolled
+//    over the stages and the ring is one K and one V object, so each lane
+//    keeps one LDS address per distinct read and reaches every stage, key
+//    block and key step through the instruction's immediate offset.  The
 //    waits for landed tiles are explicit partial vmcnt waits followed by a
 //    bare s_barrier.  16-byte chunks are XOR-swizzled per row so that the
 //    MFMA-operand reads of 16 consecutive rows hit distinct LDS banks.
@@ -98,6 +99,12 @@ struct Kernel {
         float c;
         char *kst[NSTAGE];
         char *vst[NSTAGE];
+        // LDS byte addresses of this lane's operand reads in ring stage 0,
+        // without the key block / key step (added as immediates, as is the
+        // stage): koff[kk] for the K row of d-step kk, voff[2*cb+h] for the
+        // two V^T reads of channel block cb
+        uint32_t koff[KT];
+        uint32_t voff[2 * CB];
     };
 
     // Sequence position of query row r, and the lowest / highest position
@@ -209,33 +216,64 @@ struct Kernel {
         });
     }
 
-    // V^T A-operand fragment for 16-key step ks and channel block cb: two
-    // transposing reads of 4 keys x 16 channels per 16-lane group.
-    static __device__ __forceinline__ u32x4 v_frag(const Ctx &x, const char *vl, int ks, int cb) {
+    // The per-lane read offsets of Ctx (the ring is one K and one V object,
+    // so every stage is a fixed distance from stage 0).  K: the lane reads
+    // row key_perm(l32) of each 32-key block, 16-byte chunk 2*kk + g; the
+    // swizzle depends only on the row's low four bits, which the key block
+    // does not change.  V: in each 16-lane group lane tt reads rows
+    // 8*(group/2) + tt/4 (+4) of each 16-key step at column 8*(tt%4) of its
+    // half of channel block cb; again the step does not change the low row
+    // bits.  The offsets are made opaque to the compiler so that it keeps
+    // one register each rather than one per ring stage.
+    static __device__ __forceinline__ void set_offsets(Ctx &x) {
+        const uint32_t kb0 = lds_addr(x.kst[0] + x.kgroup * TILEB);
+        const uint32_t vb0 = lds_addr(x.vst[0] + x.kgroup * TILEB);
+        const int krow = key_perm(x.l32);
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) {
+            x.koff[kk] = kb0 + (uint32_t)(krow * ROWB + (((2 * kk + x.g) ^ swz<D>(krow)) << 4));
+            asm volatile("" : "+v"(x.koff[kk]));
+        }
         const int hgrp = x.lane >> 4;
         const int tt = x.lane & 15;
-        const int row0 = ks * 16 + 8 * (hgrp >> 1) + (tt >> 2);
-        const int colb = cb * 64 + 32 * (hgrp & 1) + 8 * (tt & 3);
-        const int ch = colb >> 4, within = colb & 15;
-        const ATTN_LDS char *v0 = (const ATTN_LDS char *)vl + row0 * ROWB + ((ch ^ swz<D>(row0)) << 4) + within;
-        const ATTN_LDS char *v1 = (const ATTN_LDS char *)vl + (row0 + 4) * ROWB + ((ch ^ swz<D>(row0 + 4)) << 4) + within;
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)v0);
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)v1);
-        const u32x2 a0 = __builtin_bit_cast(u32x2, t0);
-        const u32x2 a1 = __builtin_bit_cast(u32x2, t1);
-        return u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = 8 * (hgrp >> 1) + (tt >> 2) + 4 * h;
+                const int colb = cb * 64 + 32 * (hgrp & 1) + 8 * (tt & 3);
+                const int ch = colb >> 4, within = colb & 15;
+                x.voff[2 * cb + h] = vb0 + (uint32_t)(row * ROWB + ((ch ^ swz<D>(row)) << 4) + within);
+                asm volatile("" : "+v"(x.voff[2 * cb + h]));
+            }
     }
 
-    // O^T += V^T . P^T over one tile (P_lo as well when EXACT).  The reads of
-    // step ks+1 are scheduled ahead of the MFMAs of step ks.
-    template <bool EXACT>
-    static __device__ __forceinline__ void pv(const Ctx &x, State &st, const char *vl,
-                                              const u32x4 (&ph)[QB][KS], const u32x4 (&pl)[QB][KS]) {
+    // V^T A-operand fragment of ring stage S for 16-key step ks and channel
+    // block cb: two transposing reads of 4 keys x 16 channels per 16-lane
+    // group.
+    template <int S>
+    static __device__ __forceinline__ u32x4 v_frag(const Ctx &x, int ks, int cb) {
+        constexpr int IMM0 = S * STAGEB;
+        const uint32_t a0 = x.voff[2 * cb] + (uint32_t)(IMM0 + ks * 16 * ROWB);
+        const uint32_t a1 = x.voff[2 * cb + 1] + (uint32_t)(IMM0 + ks * 16 * ROWB);
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)(uintptr_t)a0);
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4 *)(uintptr_t)a1);
+        const u32x2 b0 = __builtin_bit_cast(u32x2, t0);
+        const u32x2 b1 = __builtin_bit_cast(u32x2, t1);
+        return u32x4{b0[0], b0[1], b1[0], b1[1]};
+    }
+
+    // O^T += V^T . P^T over one tile in ring stage S (P_lo as well when
+    // EXACT).  The reads of step ks+1 are scheduled ahead of the MFMAs of
+    // step ks.
+    template <bool EXACT, int S>
+    static __device__ __forceinline__ void pv(const Ctx &x, State &st, const u32x4 (&ph)[QB][KS],
+                                              const u32x4 (&pl)[QB][KS]) {
         u32x4 va[KS][CB];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) va[ks][cb] = v_frag(x, vl, ks, cb);
+            for (int cb = 0; cb < CB; ++cb) va[ks][cb] = v_frag<S>(x, ks, cb);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -255,26 +293,17 @@ struct Kernel {
         }
     }
 
-    // Everything one wave does with one landed tile.
-    template <bool EXACT>
-    static __device__ __forceinline__ void compute_tile(const Ctx &x, State &st, int t, const char *kl,
-                                                        const char *vl) {
-        const int j0 = t * BN;
-        const int Nk = x.Nk;
-        bool edge = (j0 + BN > Nk);
-        if constexpr (MASK != MASK_NONE) edge = edge || (j0 + BN - 1 > x.pw0);
-        if constexpr (MASK == MASK_WINDOW) edge = edge || (j0 < x.w_last - x.window + 1);
-
-        // ---- S^T = K . Q^T; K fragments are read two d-steps ahead
-        f32x16 s[KB][QB];
+    // S^T = K . Q^T for the tile in ring stage S; K fragments are read two
+    // d-steps ahead.
+    template <int S>
+    static __device__ __forceinline__ void qk(const Ctx &x, const State &st, f32x16 (&s)[KB][QB]) {
         u32x4 ka[KT][KB];
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int row = kb * 32 + key_perm(x.l32);
-                const int ch = (2 * kk + x.g) ^ swz<D>(row);
-                ka[kk][kb] = *(const ATTN_LDS u32x4 *)((const ATTN_LDS char *)kl + row * ROWB + ch * 16);
+                const uint32_t a = x.koff[kk] + (uint32_t)(S * STAGEB + kb * 32 * ROWB);
+                ka[kk][kb] = *(const ATTN_LDS u32x4 *)(uintptr_t)a;
             }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -286,33 +315,68 @@ struct Kernel {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32<DT>(ka[kk][kb], st.qf[qb][kk], s[kb][qb]);
-        {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
 #pragma unroll
-            for (int kk = 0; kk < KT; ++kk) {
-                if (kk + 2 < KT) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, KB * QB, 0);
-            }
+        for (int kk = 0; kk < KT; ++kk) {
+            if (kk + 2 < KT) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, KB * QB, 0);
         }
+    }
 
-        // ---- online softmax, one lane per query row
-        u32x4 ph[QB][KS], pl[QB][KS];
+    // Does tile t need masks for some row of this wave (causal diagonal,
+    // window edge or the ragged tail)?
+    static __device__ __forceinline__ bool edge_tile(const Ctx &x, int t) {
+        const int j0 = t * BN;
+        bool edge = (j0 + BN > x.Nk);
+        if constexpr (MASK != MASK_NONE) edge = edge || (j0 + BN - 1 > x.pw0);
+        if constexpr (MASK == MASK_WINDOW) edge = edge || (j0 < x.w_last - x.window + 1);
+        return edge;
+    }
+
+    // Does some row of this wave see a key of tile t?
+    static __device__ __forceinline__ bool visible_tile(const Ctx &x, int t) {
+        bool any = x.qw0 < x.Nq;
+        if constexpr (MASK != MASK_NONE) any = any && (t * BN <= x.w_last);
+        if constexpr (MASK == MASK_WINDOW) any = any && (t * BN + BN - 1 >= x.pw0 - x.window + 1);
+        return any;
+    }
+
+    // The online-softmax update of one tile for every query block of the
+    // wave (masks on edge tiles).
+    template <bool EXACT>
+    static __device__ __forceinline__ void softmax(const Ctx &x, State &st, int t, f32x16 (&s)[KB][QB], bool edge,
+                                                   u32x4 (&ph)[QB][KS], u32x4 (&pl)[QB][KS]) {
+        const int j0 = t * BN;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int qi = x.lpos[qb];
-            int hi = Nk - 1 - (j0 + 8 * x.g);
+            int hi = x.Nk - 1 - (j0 + 8 * x.g);
             int lo = -(1 << 30);
             if constexpr (MASK != MASK_NONE) hi = min(hi, qi - (j0 + 8 * x.g));
             if constexpr (MASK == MASK_WINDOW) lo = qi - x.window + 1 - (j0 + 8 * x.g);
             f32x16 sq[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sq[kb] = s[kb][qb];
-            online_softmax<DT, KB, CB, EXACT>(sq, st.oacc[qb], st.mrun[qb], st.lsum[qb], ph[qb], pl[qb], x.c,
-                                              edge, hi, lo);
+            online_softmax<DT, KB, CB, EXACT>(sq, st.oacc[qb], st.mrun[qb], st.lsum[qb], ph[qb], pl[qb], x.c, edge,
+                                              hi, lo);
         }
+    }
+
+    // Everything one wave does with the landed tile t in ring stage S.
+    template <bool EXACT, int S>
+    static __device__ __forceinline__ void compute_tile(const Ctx &x, State &st, int t) {
+        const bool edge = edge_tile(x, t);
+
+        // ---- S^T = K . Q^T
+        f32x16 s[KB][QB];
+        qk<S>(x, st, s);
+
+        // ---- online softmax, one lane per query row
+        u32x4 ph[QB][KS], pl[QB][KS];
+        softmax<EXACT>(x, st, t, s, edge, ph, pl);
 
         // ---- O^T += V^T . P^T
-        pv<EXACT>(x, st, vl, ph, pl);
+        pv<EXACT, S>(x, st, ph, pl);
     }
 
     // One pipeline step on ring stage S: wait for tile i, barrier, prefetch
@@ -325,11 +389,7 @@ struct Kernel {
         if (i + NSTAGE - 1 < my_count) load_tile(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
         if (i < my_count) {
             const int t = my_begin + i;
-            bool any = x.qw0 < x.Nq;
-            if constexpr (MASK != MASK_NONE) any = any && (t * BN <= x.w_last);
-            if constexpr (MASK == MASK_WINDOW) any = any && (t * BN + BN - 1 >= x.pw0 - x.window + 1);
-            if (any)
-                compute_tile<EXACT>(x, st, t, x.kst[S] + x.kgroup * TILEB, x.vst[S] + x.kgroup * TILEB);
+            if (visible_tile(x, t)) compute_tile<EXACT, S>(x, st, t);
         }
     }
 
@@ -361,6 +421,7 @@ struct Kernel {
             x.kst[s] = kst[s];
             x.vst[s] = vst[s];
         }
+        set_offsets(x);
         const int N = p.N;
 
         // ---- which (batch*head, key split, query tile) this workgroup owns;
@@ -448,12 +509,11 @@ struct Kernel {
         if constexpr (MASK == MASK_WINDOW) min_vis = min(min_vis, p.window);
         const bool exact = min_vis < p.exact_below;
 
-        // ---- prologue: the first NSTAGE-1 tiles in flight
+        // ---- prologue: the first NSTAGE-1 tiles in flight, then the main
+        // loop, unrolled over the ring stages; one instance per P mode
 #pragma unroll
         for (int s = 0; s < NSTAGE - 1; ++s)
             if (s < my_count) load_tile(x, my_begin + s, x.kst[s], x.vst[s]);
-
-        // ---- main loop, unrolled over the ring stages; one instance per P mode
         if (exact)
             loop<true>(x, st, half, my_begin, my_count);
         else
@@ -590,24 +650,22 @@ template <int D, int DT, int MASK, int QB, int NWQ, int KSPLIT, int BN, int NSTA
 __global__ __launch_bounds__(NWQ * KSPLIT * 64) void attn_fwd_kernel(Params p) {
     using K = Kernel<D, DT, MASK, QB, NWQ, KSPLIT, BN, NSTAGE, PAGED>;
     constexpr int SB = K::STAGEB;
-    __shared__ __attribute__((aligned(1024))) char k0[SB];
-    __shared__ __attribute__((aligned(1024))) char v0[SB];
-    __shared__ __attribute__((aligned(1024))) char k1[SB];
-    __shared__ __attribute__((aligned(1024))) char v1[SB];
-    __shared__ __attribute__((aligned(1024))) char k2[NSTAGE > 2 ? SB : 16];
-    __shared__ __attribute__((aligned(1024))) char v2[NSTAGE > 2 ? SB : 16];
-    __shared__ __attribute__((aligned(1024))) char k3[NSTAGE > 3 ? SB : 16];
-    __shared__ __attribute__((aligned(1024))) char v3[NSTAGE > 3 ? SB : 16];
+    // one K and one V object for all ring stages: every stage is a
+    // compile-time distance from stage 0, so reads address it by immediate
+    __shared__ __attribute__((aligned(1024))) char kring[NSTAGE * SB];
+    __shared__ __attribute__((aligned(1024))) char vring[NSTAGE * SB];
     // the merge of the key groups keeps O in the ring and (m, l) here
     static_assert(KSPLIT == 1 || (D / 32 <= 2 * NSTAGE && (KSPLIT - 1) * NWQ * QB * 16 * 64 * 4 <= SB),
                   "ring too small to hold the key-group merge");
+    static_assert((NSTAGE - 1) * SB + (BN - 16) * D * 2 < 65536, "stage offsets must fit the 16-bit LDS immediate");
     __shared__ __attribute__((aligned(16))) float ml[KSPLIT > 1 ? (KSPLIT - 1) * NWQ * QB * 2 * 64 : 4];
     char *kst[NSTAGE];
     char *vst[NSTAGE];
-    kst[0] = k0; vst[0] = v0;
-    kst[1] = k1; vst[1] = v1;
-    if constexpr (NSTAGE > 2) { kst[2] = k2; vst[2] = v2; }
-    if constexpr (NSTAGE > 3) { kst[3] = k3; vst[3] = v3; }
+#pragma unroll
+    for (int s = 0; s < NSTAGE; ++s) {
+        kst[s] = kring + s * SB;
+        vst[s] = vring + s * SB;
+    }
     K::run(p, kst, vst, ml);
 }
 
