@@ -21,12 +21,11 @@ SOURCES = [
     (os.path.join(CSRC, "attn_fwd_paged64.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_fwd_paged128.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
     (os.path.join(CSRC, "attn_bwd.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
-    (os.path.join(CSRC, "attn_fwd_pp.hip"), ["-Rpass-analysis=kernel-resource-usage"]),
 ]
 # Kernels whose loads are tracked by explicit vmcnt waits must not touch
 # scratch memory (a spill reload would count as an outstanding load).
-NO_SCRATCH = ("attn_fwd_kernel", "attn_fwd_pp_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel")
-HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp", "attn_fwd_pp.hpp",
+NO_SCRATCH = ("attn_fwd_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel")
+HEADERS = [os.path.join(CSRC, f) for f in ("attn_fwd_common.hpp", "attn_fwd_kernel.hpp",
                                             "attn_fwd_launch.hpp",
                                             "attn_fwd_merge.hpp", "attn_fwd_lockstep.hpp")] + [
     os.path.join(INCLUDE, "attn_fwd.h"), os.path.join(INCLUDE, "attn_bwd.h")]

@@ -19,45 +19,35 @@ namespace {
 
 using attnfwd::Params;
 
-// Tile configurations compiled into the library.  qb: 32-row query blocks
-// per wave; nwq: query waves per workgroup; ksplit: key groups per workgroup
-// (2 or 4 = further sets of waves take later parts of the key range, merged
-// in LDS); bn: keys per K/V tile; nstage: depth of the LDS tile ring; kind: 0
-// = lockstep kernel (attn_fwd_kernel.hpp), 1 = ping-pong kernel
-// (attn_fwd_pp.hpp: two groups of four waves own 128 rows each and alternate
-// matrix and vector phases).  The same id may use a smaller tile for d = 128
-// so that LDS and registers fit.
+// Tile configurations compiled into the library (all of the lockstep kernel,
+// attn_fwd_kernel.hpp).  qb: 32-row query blocks per wave; nwq: query waves
+// per workgroup; ksplit: key groups per workgroup (2 or 4 = further sets of
+// waves take later parts of the key range, merged in LDS); bn: keys per K/V
+// tile; nstage: depth of the LDS tile ring.  The same id may use a smaller
+// tile for d = 128 so that LDS and registers fit.  Each is the automatic
+// choice of some workload (see auto_config and splitkv_auto_config).
 struct TileCfg {
-    int qb, nwq, ksplit, bn, nstage, kind;
+    int qb, nwq, ksplit, bn, nstage;
     int bm() const { return qb * nwq * 32; }
     int waves() const { return nwq * ksplit; }
 };
-constexpr int kNumConfigs = 8;
-constexpr int kPingPong = 4;
+constexpr int kNumConfigs = 5;
 constexpr TileCfg kCfg64[kNumConfigs] = {
-    {1, 4, 1, 64, 3, 0},   // 0: 128 rows, 4 waves
-    {1, 4, 2, 64, 3, 0},   // 1: 128 rows, 8 waves (two key groups)
-    {1, 8, 1, 64, 3, 0},   // 2: 256 rows, 8 waves
-    {2, 4, 1, 64, 3, 0},   // 3: 256 rows, 4 waves with 64 rows each
-    {1, 8, 1, 64, 4, 1},   // 4: ping-pong, 256 rows in two groups of four waves
-    {1, 2, 2, 64, 2, 0},   // 5: 64 rows, 4 waves (two key groups), two workgroups per CU
-    {1, 1, 1, 64, 3, 0},   // 6: 32 rows, 1 wave (few query rows: decoding)
-    {1, 1, 4, 64, 2, 0},   // 7: 32 rows, 4 waves in four key groups (small grids)
+    {1, 4, 2, 64, 3},   // 0: 128 rows, 8 waves (two key groups)
+    {1, 8, 1, 64, 3},   // 1: 256 rows, 8 waves
+    {1, 2, 2, 64, 2},   // 2: 64 rows, 4 waves (two key groups), two workgroups per CU
+    {1, 1, 1, 64, 3},   // 3: 32 rows, 1 wave (few query rows: decoding)
+    {1, 1, 4, 64, 2},   // 4: 32 rows, 4 waves in four key groups (small grids)
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
-    {1, 4, 1, 64, 3, 0},
-    {1, 4, 2, 64, 2, 0},
-    {1, 8, 1, 64, 3, 0},
-    {2, 4, 1, 32, 3, 0},
-    {1, 8, 1, 64, 4, 1},
-    {1, 2, 2, 32, 2, 0},
-    {1, 1, 1, 32, 3, 0},
-    {1, 1, 4, 32, 2, 0},
+    {1, 4, 2, 64, 2},
+    {1, 8, 1, 64, 3},
+    {1, 2, 2, 32, 2},
+    {1, 1, 1, 32, 3},
+    {1, 1, 4, 32, 2},
 };
 const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg128[id]; }
 
-// Every configuration is built for both head dims.
-bool cfg_built(int64_t, int) { return true; }
 
 // Query tiles whose first row sees fewer keys than this use the two-term P.
 constexpr int kExactBelow = 256;
@@ -88,23 +78,22 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int ca
 }
 
 // Automatic choice (measured on MI355X).  d = 128 with at least two 256-row
-// workgroups per compute unit runs 8 query waves of 32 rows (2); smaller
-// d = 128 grids run 128-row workgroups with two key groups (1).  The
-// ping-pong kernel (4) measured slower than 2 on every prefill workload.  For d = 64, 64-row
-// workgroups, two per compute unit (5), win on small grids and on masked
-// runs, where they spread the uneven causal work over twice as many
-// workgroups; larger unmasked grids keep the 128-row workgroups (1).  When
+// workgroups per compute unit runs 8 query waves of 32 rows (1); smaller
+// d = 128 grids run 128-row workgroups with two key groups (0).  For d = 64,
+// 64-row workgroups, two per compute unit (2), win on small grids and on
+// masked runs, where they spread the uneven causal work over twice as many
+// workgroups; larger unmasked grids keep the 128-row workgroups (0).  When
 // even 32-row workgroups are at most one per compute unit, 32 rows with four
-// key groups (7) keep every SIMD busy.
+// key groups (4) keep every SIMD busy.
 int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask) {
     const int64_t wg128 = B * Hq * ((N + 127) / 128);
     if (d == 128) {
         const int64_t wg256 = B * Hq * ((N + 255) / 256);
-        return wg256 >= 512 ? 2 : 1;
+        return wg256 >= 512 ? 1 : 0;
     }
-    if (B * Hq * ((N + 31) / 32) <= 256) return 7;
-    if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 5 : 1;
-    return wg128 < 128 ? 5 : 1;
+    if (B * Hq * ((N + 31) / 32) <= 256) return 4;
+    if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 2 : 0;
+    return wg128 < 128 ? 2 : 0;
 }
 
 // Routes a launch to the translation unit that holds its instantiation.
@@ -114,7 +103,6 @@ hipError_t launch(int64_t d, int dtype, int mask, int cfg, const Params &p, int6
     if (p.paged)
         return d == 64 ? attnfwd::launch_lockstep_paged64(dt, mask, cfg, p, grid, stream)
                        : attnfwd::launch_lockstep_paged128(dt, mask, cfg, p, grid, stream);
-    if (cfg == kPingPong) return attnfwd::launch_pingpong(d, dt, mask, p, grid, stream);
     if (d == 64) return attnfwd::launch_lockstep_d64(dt, mask, cfg, p, grid, stream);
     return attnfwd::launch_lockstep_d128(dt, mask, cfg, p, grid, stream);
 }
@@ -235,18 +223,17 @@ KvView kv_view(int64_t Hq, int64_t Hkv, int64_t Nq) {
 }
 
 // Automatic choice for split-KV calls (from measurement): one-wave 32-row
-// workgroups while a (stacked) head has fewer than 32 rows (GQA decoding: few
-// rows, many K/V heads, so many workgroups); at 32 rows and more, with few
-// K/V heads (MQA decoding), the 8-wave workgroups of configuration 1 keep
+// workgroups (3) while a (stacked) head has fewer than 32 rows (GQA decoding:
+// few rows, many K/V heads, so many workgroups); at 32 rows and more, with few
+// K/V heads (MQA decoding), the 8-wave workgroups of configuration 0 keep
 // more loads in flight per compute unit; longer query blocks take the choice
-// of the plain forward, with 64-row workgroups (7) in place of the four-key-
-// group ones (9): key chunks already spread a small grid.
+// of the plain forward, with 64-row workgroups (2) in place of the four-key-
+// group ones (4): key chunks already spread a small grid.
 int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask) {
-    if (Nq < 32) return 6;
-    if (Nq <= 128) return 1;
+    if (Nq < 32) return 3;
+    if (Nq <= 128) return 0;
     const int id = auto_config(B, Hq, Nq, d, mask);
-    if (id == 7) return 5;
-    return id == kPingPong ? 2 : id;
+    return id == 4 ? 2 : id;
 }
 
 struct SplitPlan {
@@ -338,7 +325,6 @@ int attn_fwd_num_configs(void) { return kNumConfigs; }
 
 int attn_fwd_config_desc(int id, int64_t d, int64_t *desc) {
     if (id < 0 || id >= kNumConfigs || !desc || (d != 64 && d != 128)) return ATTN_ERR_ARG;
-    if (!cfg_built(d, id)) return ATTN_ERR_UNSUPPORTED;
     const TileCfg &tc = tile_cfg(d, id);
     desc[0] = tc.qb;
     desc[1] = tc.waves();
@@ -354,7 +340,6 @@ int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
     const int rc = check_sizes(B, Hq, Hkv, N, d, causal, window, 1.0f, dtype);
     if (rc != ATTN_OK) return rc;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
-    if (config_id >= 0 && !cfg_built(d, config_id)) return ATTN_ERR_UNSUPPORTED;
     const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d, mask_mode(causal, window));
     const TileCfg &tc = tile_cfg(d, id);
     if (cfg) {
@@ -384,7 +369,6 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     int rc = attn_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype);
     if (rc != ATTN_OK) return rc;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
-    if (config_id >= 0 && !cfg_built(d, config_id)) return ATTN_ERR_UNSUPPORTED;
     if (N == 0) return ATTN_OK;
 
     const int id = config_id >= 0 ? config_id : auto_config(B, Hq, N, d, mask_mode(causal, window));
@@ -397,28 +381,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     const int mask = mask_mode(causal, window);
     Params p = make_params(q, k, v, o, lse, B, Hq, Hkv, N, N, window, mask, scale, ntiles);
     // two 64-row workgroups share a compute unit: pair heavy and light tiles
-    p.zigzag = (id == 5) ? 1 : 0;
-
-    hipError_t err = hipSuccess;
-    if (tc.kind == 1) {
-        // The ping-pong kernel has no two-term-P path: the leading query
-        // tiles whose first row sees few keys (a prefix in tile order) run on
-        // the lockstep kernel with the same 256-row tiling (configuration 2),
-        // the rest on the ping-pong kernel, which takes its tiles from the
-        // last down, so n_qtiles keeps its meaning there.  Unmasked calls
-        // have such tiles only when N is below the threshold, and then every
-        // tile is one.  The two launches write disjoint rows.
-        const int64_t n_exact = exact_tiles(N, causal, mask == attnfwd::MASK_WINDOW ? p.window : 0, bm);
-        const int64_t n_pp = (mask == attnfwd::MASK_NONE && n_exact > 0) ? 0 : ntiles - n_exact;
-        if (n_pp < ntiles) {
-            Params pe = p;
-            pe.n_qtiles = (int)(ntiles - n_pp);
-            err = launch(d, dtype, mask, 2, pe, B * Hq * (ntiles - n_pp), (hipStream_t)stream);
-        }
-        if (err == hipSuccess && n_pp > 0) err = launch(d, dtype, mask, id, p, B * Hq * n_pp, (hipStream_t)stream);
-    } else {
-        err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
-    }
+    p.zigzag = (id == 2) ? 1 : 0;
+    const hipError_t err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
     return status_of(err);
 }
 
@@ -440,7 +404,6 @@ int attn_fwd_splitkv_validate(const void *q, const void *k, const void *v, const
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
     const KvView kv = kv_view(Hq, Hkv, Nq);
     const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
-    if (tile_cfg(d, id).kind != 0) return ATTN_ERR_UNSUPPORTED;
     const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)workspace;
     if ((mis & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_ALIGN;
     if (Nq == 0) return ATTN_OK;
@@ -479,7 +442,6 @@ int attn_fwd_splitkv_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_
     const KvView kv = kv_view(Hq, Hkv, Nq);
     const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
     const TileCfg &tc = tile_cfg(d, id);
-    if (tc.kind != 0) return ATTN_ERR_UNSUPPORTED;
     const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, Nk, Nk - Nq, causal, window, d, num_splits, id);
     if (plan) {
         plan[0] = tc.bm();
@@ -521,7 +483,7 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
                            scale, sp.ntiles);
     p.q_off = (int)(Nk - Nq);
     p.pack_nq = kv.pack_nq;
-    p.zigzag = (id == 5) ? 1 : 0;
+    p.zigzag = (id == 2) ? 1 : 0;
     p.n_splits = (int)sp.n_splits;
     p.split_tiles = (int)sp.split_tiles;
     p.split_t0 = (int)sp.t0;
@@ -629,7 +591,6 @@ int attn_fwd_autotune(const void *q, const void *k, const void *v, void *o, floa
     float best = -1.0f;
     rc = ATTN_OK;
     for (int id = 0; id < kNumConfigs && rc == ATTN_OK; ++id) {
-        if (!cfg_built(d, id)) continue;
         // one untimed call, then `reps` back-to-back calls between two events
         rc = attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, dtype, id, stream);
         if (rc != ATTN_OK) break;
@@ -674,7 +635,6 @@ int attn_fwd_paged_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
     const KvView kv = kv_view(Hq, Hkv, Nq);
     const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
     const TileCfg &tc = tile_cfg(d, id);
-    if (tc.kind != 0) return ATTN_ERR_UNSUPPORTED;
     // lengths differ per batch: chunks cover [0, max_seq_len)
     const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, max_seq_len, 0, 0, 0, d, num_splits, id);
     if (plan) {
@@ -764,7 +724,7 @@ int attn_fwd_paged_ex(const void *q, const void *k_pool, const void *v_pool, con
                            window, mask, scale, sp.ntiles);
     p.q_off = (int)(max_seq_len - Nq);   // replaced per batch from seq_lens in the kernel
     p.pack_nq = kv.pack_nq;
-    p.zigzag = (id == 5) ? 1 : 0;
+    p.zigzag = (id == 2) ? 1 : 0;
     p.n_splits = (int)sp.n_splits;
     p.split_tiles = (int)sp.split_tiles;
     p.split_t0 = 0;

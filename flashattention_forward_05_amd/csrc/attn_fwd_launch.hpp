@@ -9,13 +9,9 @@
 
 namespace attnfwd {
 
-// The ping-pong kernel (tile configuration 4, attn_fwd_pp.hpp) for head dim d
-// (64 or 128), dtype dt (0 = fp16, 1 = bf16) and mask mode.
-hipError_t launch_pingpong(int64_t d, int dt, int mask, const Params &p, int64_t grid, hipStream_t stream);
-
-// Lockstep-kernel configurations (ids 0, 1, 2, 3, 5, 6, 7) in their own
-// translation units: contiguous K/V at head dim 64 and 128, and paged K/V at
-// head dim 64 and 128.
+// Lockstep-kernel configurations (ids 0 .. 4), dtype dt (0 = fp16, 1 = bf16)
+// and mask mode, in their own translation units: contiguous K/V at head dim
+// 64 and 128, and paged K/V at head dim 64 and 128.
 hipError_t launch_lockstep_d64(int dt, int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream);
 hipError_t launch_lockstep_d128(int dt, int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream);
 hipError_t launch_lockstep_paged64(int dt, int mask, int cfg, const Params &p, int64_t grid, hipStream_t stream);

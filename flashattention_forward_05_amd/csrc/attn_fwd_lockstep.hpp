@@ -18,19 +18,17 @@ hipError_t launch_lockstep_one(const Params &p, int64_t grid, hipStream_t stream
                            dim3((unsigned)grid), dim3(NWQ * KSPLIT * 64), argv, 0, stream);
 }
 
-// Configuration ids 0, 1, 2, 3, 5, 6, 7 (the table in attn_fwd.hip); any other id
-// is hipErrorInvalidValue.
+// Configuration ids 0 .. 4 (the table in attn_fwd.hip); any other id is
+// hipErrorInvalidValue.
 template <int D, int DT, int MASK, bool PAGED>
 hipError_t launch_lockstep_cfg(int cfg, const Params &p, int64_t grid, hipStream_t stream) {
     constexpr bool small = D == 64;
     switch (cfg) {
-    case 0: return launch_lockstep_one<D, DT, MASK, 1, 4, 1, 64, 3, PAGED>(p, grid, stream);
-    case 1: return launch_lockstep_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2, PAGED>(p, grid, stream);
-    case 2: return launch_lockstep_one<D, DT, MASK, 1, 8, 1, 64, 3, PAGED>(p, grid, stream);
-    case 3: return launch_lockstep_one<D, DT, MASK, 2, 4, 1, small ? 64 : 32, 3, PAGED>(p, grid, stream);
-    case 5: return launch_lockstep_one<D, DT, MASK, 1, 2, 2, small ? 64 : 32, 2, PAGED>(p, grid, stream);
-    case 6: return launch_lockstep_one<D, DT, MASK, 1, 1, 1, small ? 64 : 32, 3, PAGED>(p, grid, stream);
-    case 7: return launch_lockstep_one<D, DT, MASK, 1, 1, 4, small ? 64 : 32, 2, PAGED>(p, grid, stream);
+    case 0: return launch_lockstep_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2, PAGED>(p, grid, stream);
+    case 1: return launch_lockstep_one<D, DT, MASK, 1, 8, 1, 64, 3, PAGED>(p, grid, stream);
+    case 2: return launch_lockstep_one<D, DT, MASK, 1, 2, 2, small ? 64 : 32, 2, PAGED>(p, grid, stream);
+    case 3: return launch_lockstep_one<D, DT, MASK, 1, 1, 1, small ? 64 : 32, 3, PAGED>(p, grid, stream);
+    case 4: return launch_lockstep_one<D, DT, MASK, 1, 1, 4, small ? 64 : 32, 2, PAGED>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -120,9 +120,10 @@ int attn_fwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int 
  * desc[0..5] = {32-row query blocks per wave, waves per workgroup, keys per
  * K/V tile, query rows per workgroup, key groups per workgroup, depth of the
  * LDS tile ring}.  attn_fwd_config_desc returns ATTN_ERR_ARG for a bad id, a
- * bad d or a NULL desc, and ATTN_ERR_UNSUPPORTED for a configuration not built
- * for that d (every id is built for d = 64 and d = 128; id 4 is the two-group
- * ping-pong kernel, the others the lockstep kernel).
+ * bad d or a NULL desc.  Every id is built for d = 64 and d = 128: 0 = 128
+ * query rows in 8 waves (two key groups), 1 = 256 rows in 8 waves, 2 = 64
+ * rows in 4 waves (two key groups), 3 = 32 rows in one wave, 4 = 32 rows in 4
+ * waves (four key groups).
  */
 int attn_fwd_num_configs(void);
 int attn_fwd_config_desc(int id, int64_t d, int64_t *desc);
@@ -138,8 +139,7 @@ int attn_fwd_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
  * attn_fwd with an explicit tile configuration (config_id in
  * [0, attn_fwd_num_configs()), or -1 for the automatic choice that attn_fwd
  * makes).  Same semantics, layout, ownership and errors as attn_fwd, plus
- * ATTN_ERR_ARG for a bad config_id and ATTN_ERR_UNSUPPORTED for one not built
- * for this d (attn_fwd_config_desc says which).  Every configuration computes the same
+ * ATTN_ERR_ARG for a bad config_id.  Every configuration computes the same
  * function; they differ only in speed.
  */
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -215,8 +215,7 @@ int attn_fwd_autotune(const void *q, const void *k, const void *v, void *o, floa
  * is launched and o, lse and the workspace are untouched): those of attn_fwd
  * with N read as Nq, plus ATTN_ERR_SHAPE for Nk < 0, Nk == 0 < Nq or causal
  * with Nq > Nk; ATTN_ERR_ARG for num_splits outside [0, 1024] or a bad
- * config_id; ATTN_ERR_UNSUPPORTED for a configuration of a kernel kind other
- * than the lockstep one (id 4, the ping-pong kernel); ATTN_ERR_NULL for a NULL workspace
+ * config_id; ATTN_ERR_NULL for a NULL workspace
  * when more than one chunk is used; ATTN_ERR_WORKSPACE when workspace_bytes
  * is too small; ATTN_ERR_ALIGN for a misaligned workspace; ATTN_ERR_ALIAS when
  * it overlaps an input or output.  Enqueues two kernels (attention, then the
@@ -229,9 +228,9 @@ int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float
 
 /* attn_fwd_splitkv with an explicit tile configuration (-1 = automatic: with
  * R query rows per head as launched -- G * Nq when the heads are stacked, see
- * attn_fwd_splitkv_plan -- configuration 6, one-wave 32-row workgroups, for
- * R < 32; configuration 1 for 32 <= R <= 128; else the choice attn_fwd
- * makes, with configuration 5 in place of 7 and 2 in place of 4). */
+ * attn_fwd_splitkv_plan -- configuration 3, one-wave 32-row workgroups, for
+ * R < 32; configuration 0 for 32 <= R <= 128; else the choice attn_fwd
+ * makes, with configuration 2 in place of 4). */
 int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, float *lse,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                         int causal, int64_t window, float scale, int dtype, int64_t num_splits,

@@ -115,17 +115,17 @@ def test_auto_config_choice():
     workgroups for large unmasked grids; 256-row workgroups for large d=128
     grids."""
     auto = lambda *a: fa.attn_fwd_plan_ex(*a, -1)["config_id"]
-    assert auto(2, 4, 4, 4096, 64, 1, 0, 0) == 5        # lab, causal
-    assert auto(2, 4, 4, 4096, 64, 0, 0, 0) == 1        # lab, full
-    assert auto(2, 4, 4, 1024, 64, 0, 0, 0) == 7        # small grid: 32 rows, four key groups
-    assert auto(2, 4, 4, 1024, 64, 1, 0, 0) == 7
-    assert auto(2, 4, 4, 256, 64, 1, 0, 0) == 7
-    assert auto(2, 4, 4, 2048, 64, 1, 0, 0) == 5        # 512 32-row workgroups
-    assert auto(1, 12, 12, 2048, 64, 0, 0, 0) == 1      # stress, full
-    assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 5      # stress, causal
-    assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 2      # GQA prefill
-    assert auto(1, 32, 1, 32768, 128, 1, 4096, 1) == 2  # MQA with window
-    assert auto(1, 2, 2, 512, 128, 1, 0, 1) == 1        # small d=128 grid
+    assert auto(2, 4, 4, 4096, 64, 1, 0, 0) == 2        # lab, causal
+    assert auto(2, 4, 4, 4096, 64, 0, 0, 0) == 0        # lab, full
+    assert auto(2, 4, 4, 1024, 64, 0, 0, 0) == 4        # small grid: 32 rows, four key groups
+    assert auto(2, 4, 4, 1024, 64, 1, 0, 0) == 4
+    assert auto(2, 4, 4, 256, 64, 1, 0, 0) == 4
+    assert auto(2, 4, 4, 2048, 64, 1, 0, 0) == 2        # 512 32-row workgroups
+    assert auto(1, 12, 12, 2048, 64, 0, 0, 0) == 0      # stress, full
+    assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 2      # stress, causal
+    assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 1      # GQA prefill
+    assert auto(1, 32, 1, 32768, 128, 1, 4096, 1) == 1  # MQA with window
+    assert auto(1, 2, 2, 512, 128, 1, 0, 1) == 0        # small d=128 grid
 
 
 # ---- split-KV entry points (host checks, plan, workspace size)
@@ -152,8 +152,8 @@ def validate_kv(**over):
     ({"causal": 0, "Nq": 5000}, 0),                                     # non-causal may have Nq > Nk
     ({"q": None}, 1), ({"workspace": None}, 1),
     ({"Nk": 0}, 2), ({"Nk": -1}, 2), ({"Nq": 4097}, 2), ({"Nk": (1 << 24) + 1}, 2), ({"Hq": 3}, 2),
-    ({"d": 96}, 3), ({"config_id": 4}, 3), ({"window": 8, "causal": 0}, 3),
-    ({"num_splits": -1}, 4), ({"num_splits": 1025}, 4), ({"config_id": 8}, 4), ({"scale": float("nan")}, 4),
+    ({"d": 96}, 3), ({"window": 8, "causal": 0}, 3), ({"config_id": 4}, 0),
+    ({"num_splits": -1}, 4), ({"num_splits": 1025}, 4), ({"config_id": 5}, 4), ({"scale": float("nan")}, 4),
     ({"workspace": 6 * G + 8}, 5), ({"q": G + 2}, 5),
     ({"o": 2 * G}, 6), ({"workspace": 3 * G}, 6), ({"workspace": 5 * G}, 6), ({"workspace": 4 * G - 64}, 6),
     ({"workspace_bytes": 64}, 9),
@@ -166,7 +166,7 @@ def test_splitkv_plan_and_workspace():
     # decoding: the 4 query heads of each K/V head stacked into one 32-row
     # workgroup per chunk, automatic chunk count
     p = fa.attn_fwd_splitkv_plan(4, 32, 8, 1, 8192, 128, 1, 0, 1)
-    assert p["config_id"] == 6 and p["block_m"] == 32 and p["waves"] == 1 and p["stacked"] == 1
+    assert p["config_id"] == 3 and p["block_m"] == 32 and p["waves"] == 1 and p["stacked"] == 1
     key_tiles = 8192 // p["block_n"]
     assert p["n_splits"] > 1 and p["split_tiles"] >= 4
     assert p["n_splits"] == -(-key_tiles // p["split_tiles"])
@@ -192,7 +192,7 @@ def test_splitkv_plan_and_workspace():
     # square prefill shapes take the plain forward's tile choice and, on grids
     # of 64 workgroups or more, one chunk
     assert fa.attn_fwd_splitkv_plan(2, 4, 4, 1024, 1024, 64, 1, 0, 0)["n_splits"] == 1
-    assert fa.attn_fwd_splitkv_plan(2, 4, 4, 1024, 1024, 64, 1, 0, 0)["config_id"] == 5
+    assert fa.attn_fwd_splitkv_plan(2, 4, 4, 1024, 1024, 64, 1, 0, 0)["config_id"] == 2
     with pytest.raises(fa.AttnError) as e:                       # the C call returns -status
         fa.attn_fwd_splitkv_workspace_size(1, 3, 2, 1, 10, 64, 1, 0, 0)
     assert e.value.status == 2
@@ -222,7 +222,7 @@ def validate_pg(**over):
     ({"bt": None}, 1), ({"sl": None}, 1), ({"kp": None}, 1), ({"workspace": None}, 1),
     ({"max_seq_len": 4097}, 2), ({"max_seq_len": 0}, 2), ({"num_pages": 0}, 2), ({"max_pages": 0}, 2),
     ({"page_size": 4}, 3), ({"page_size": 24}, 3), ({"page_size": 512, "max_pages": 8}, 3), ({"d": 96}, 3),
-    ({"config_id": 4}, 3),
+    ({"config_id": 4}, 0), ({"config_id": 5}, 4),
     ({"num_splits": -1}, 4),
     ({"bt": 4 * G + 2}, 5), ({"sl": 4 * G + (1 << 20) + 1}, 5), ({"workspace": 7 * G + 4}, 5),
     ({"o": 2 * G + 64}, 6), ({"lse": 4 * G}, 6), ({"workspace": 3 * G}, 6), ({"workspace": 4 * G + (1 << 20)}, 6),
