@@ -216,12 +216,29 @@ def oracle_bwd_rows(q, k, v, dout, row_ids, *, scale: float, causal: bool = Fals
     return dq
 
 
+def _rows_seeing(keys_local, N: int, causal: bool, window: int) -> np.ndarray:
+    """Query positions i (of a square N x N problem) that see at least one of
+    the given key positions: every row without a mask; rows i >= j with the
+    causal mask, and i < j + window with a window (visibility of the forward:
+    0 <= i - j < window)."""
+    if not causal:
+        return np.arange(N, dtype=np.int64)
+    seen = np.zeros(N, dtype=bool)
+    for j in np.unique(keys_local):
+        hi = N if window <= 0 else min(N, int(j) + window)
+        seen[int(j):hi] = True
+    return np.nonzero(seen)[0].astype(np.int64)
+
+
 def oracle_bwd_keys(q, k, v, dout, key_ids, *, scale: float, causal: bool = False, window: int = 0,
                     dtype: str = "f16", lib: ctypes.CDLL | None = None):
     """dk and dv of selected keys (flat (b*Hkv + hk)*N + j), float64 (n, d)
-    each.  For every (batch, K/V head) that holds a selected key, runs the
-    oracle's own forward over that group's query heads first, for each row's
-    log-sum-exp and output, from which the Jacobian term D = sum(dout * O)."""
+    each.  A key's gradients need, for every query row that sees it, the row's
+    log-sum-exp and the Jacobian term D = sum(dout * O); for each (batch, K/V
+    head) that holds a selected key this forms them with the oracle's own
+    forward over exactly those rows of that group's query heads (all rows
+    without a mask; with a causal mask only rows at or after the earliest
+    selected key, which keeps full-size checks of late keys cheap)."""
     lib = lib or load_library()
     q, k, v, dout = (_as_input(x, dtype) for x in (q, k, v, dout))
     B, Hq, Hkv, Nq, Nk, d = _check_shapes(q, k, v)
@@ -237,20 +254,26 @@ def oracle_bwd_keys(q, k, v, dout, key_ids, *, scale: float, causal: bool = Fals
     for grp in np.unique(ids // N):
         b, hk = divmod(int(grp), Hkv)
         sel = np.nonzero(ids // N == grp)[0]
+        local = np.ascontiguousarray(ids[sel] % N)
         qs = np.ascontiguousarray(q[b:b + 1, hk * G:(hk + 1) * G])
         dos = np.ascontiguousarray(dout[b:b + 1, hk * G:(hk + 1) * G])
         ks = np.ascontiguousarray(k[b:b + 1, hk:hk + 1])
         vs = np.ascontiguousarray(v[b:b + 1, hk:hk + 1])
-        o, lse = oracle_fwd(qs, ks, vs, scale=scale, causal=causal, window=window, dtype=dtype, lib=lib)
+        pos = _rows_seeing(local, N, causal, window)
+        rows = (np.arange(G, dtype=np.int64)[:, None] * N + pos[None, :]).reshape(-1)
+        o, lse_rows = oracle_rows(qs, ks, vs, rows, scale=scale, causal=causal, window=window, dtype=dtype,
+                                  lib=lib)
         if dtype == "f64":
-            dof = dos
+            dof = dos.reshape(G * N, d)[rows]
         else:
             if table is None:
                 table = np.array([lib.attn_oracle_decode(x, DTYPES[dtype]) for x in range(65536)], np.float64)
-            dof = table[dos]
-        drow = np.ascontiguousarray((dof * o).sum(-1))
-        lse = np.ascontiguousarray(lse)
-        local = np.ascontiguousarray(ids[sel] % N)
+            dof = table[dos.reshape(G * N, d)[rows]]
+        # the key routine reads lse and D only at rows that see a selected key
+        lse = np.full(G * N, np.nan)
+        drow = np.full(G * N, np.nan)
+        lse[rows] = lse_rows
+        drow[rows] = (dof * o).sum(-1)
         gk = np.zeros((sel.shape[0], d), np.float64)
         gv = np.zeros((sel.shape[0], d), np.float64)
         rc = lib.attn_oracle_bwd_keys(qs.ctypes.data, ks.ctypes.data, vs.ctypes.data, dos.ctypes.data,

@@ -202,3 +202,44 @@ def test_bwd_mqa_n32768_properties(fa, window):
     assert rel < TOL_BWD[dtype], f"{label}: dq error {rel:.2e} x max|ref|"
     assert (err_dv < bound_dv).all(), f"{label}: sum of dv differs from the sum of dO"
     assert (err_dk < bound_dk).all(), f"{label}: sum of dk is not 0"
+
+
+# ---- MQA long context at full size, key by key: dk and dv of keys in the
+# last 136 positions (both sides of the last 128- and 64-key block edges),
+# checked elementwise.  Only the query rows at or after the earliest of them
+# see these keys, so the oracle forms just those rows' normalisers (32 heads x
+# 136 rows) instead of the whole forward.
+@pytest.mark.timeout(400)
+def test_bwd_mqa_n32768_keys(fa):
+    B, Hq, Hkv, N, d, dtype = 1, 32, 1, 32768, 128, "bf16"
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, dtype, seed=0)
+    do = make_dout(B, Hq, N, d, dtype, seed=0)
+    label = f"bwd MQA (1, 32/1, 32768, 128) bf16 causal, late keys"
+    say(f"case {label}")
+    dq, dk, dv = run_bwd(q, k, v, do, causal=True)
+    rng = np.random.default_rng(11)
+    edges = [N - 136, N - 129, N - 128, N - 127, N - 65, N - 64, N - 63, N - 33, N - 32, N - 2, N - 1]
+    keys = np.unique(np.concatenate([edges, rng.integers(N - 136, N, 20)]))
+    assert keys.size >= 24
+    s = float(np.float32(1.0 / math.sqrt(d)))
+    bits = [to_bits(t) for t in (q, k, v, do)]
+    say(f"  oracle for {keys.size} keys")
+    rk, rv = oracle.oracle_bwd_keys(*bits, keys, scale=s, causal=True, window=0, dtype=dtype)
+    gk = dk.reshape(-1, d)[keys].to(torch.float64).numpy()
+    gv = dv.reshape(-1, d)[keys].to(torch.float64).numpy()
+    assert np.isfinite(gk).all() and np.isfinite(gv).all(), f"{label}: non-finite dk or dv"
+    assert np.abs(rk).max() > 0 and np.abs(gk).max() > 0, f"{label}: dk is all zero"
+    ek = float(np.abs(gk - rk).max() / np.abs(rk).max())
+    ev = float(np.abs(gv - rv).max() / np.abs(rv).max())
+    say(f"  {label}: {keys.size} keys, max error / max|ref|: dk {ek:.2e}, dv {ev:.2e} (tol {TOL_BWD[dtype]:.2e})")
+    assert ek < TOL_BWD[dtype], f"{label}: dk error {ek:.2e} x max|ref|"
+    assert ev < TOL_BWD[dtype], f"{label}: dv error {ev:.2e} x max|ref|"
+
+
+# ---- d=64 on a grid of at least 512 128-row workgroups (B*Hq*ceil(N/128)),
+# ragged N, causal and not, sampled rows and keys against the oracle
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d64_large_grid_sampled(fa, causal):
+    B, Hq, Hkv, N = 4, 16, 4, 1000
+    assert B * Hq * -(-N // 128) >= 512
+    sampled_case(B, Hq, Hkv, N, 64, "f16", causal, seed=5, n_rows=48, n_keys=24)
