@@ -275,7 +275,7 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], f32x16 (&o)[CB],
                                                bool edge, int hi, int lo) {
     if constexpr (!EXACT) {
         if (!edge && __builtin_amdgcn_ballot_w64(m == -__builtin_inff()) == 0) {
-            float rs = 0.0f;
+            float rs = 0.0f, rs1 = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 2 * KB; ++ks) {
                 const int kb = ks / 2, r0 = 8 * (ks % 2);
@@ -283,11 +283,25 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], f32x16 (&o)[CB],
                 for (int q = 0; q < 4; ++q) {
                     const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * q], c, -m));
                     const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * q + 1], c, -m));
-                    rs += e0;
-                    rs += e1;
-                    ph[ks][q] = pack2<DT>(e0, e1);
+                    const uint32_t pk = pack2<DT>(e0, e1);
+                    ph[ks][q] = pk;
+                    if constexpr (DT == 0) {
+                        // fp16: sum the packed pair with one dot product
+                        // against (1, 1); the rounding of p moves the row's
+                        // log-sum-exp by at most the fp16 unit roundoff.  The
+                        // pair is taken from the scalar pk: this compiler
+                        // miscompiles __builtin_bit_cast of an element of an
+                        // ext_vector_type lvalue (it reads element 0).
+                        float &acc = (q & 1) ? rs1 : rs;
+                        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
+                                                     __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+                    } else {
+                        rs += e0;
+                        rs += e1;
+                    }
                 }
             }
+            rs += rs1;
             if (__builtin_amdgcn_ballot_w64(!(rs <= 32768.0f)) == 0) {
                 l += rs;
                 return;
