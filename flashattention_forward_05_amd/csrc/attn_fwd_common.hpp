@@ -91,6 +91,29 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
     }
 }
 
+// 2^x on the FMA pipe instead of the transcendental unit: x = n + f with
+// n = floor(x) and f in [0, 1) (Cody and Waite's argument reduction), 2^f by
+// a cubic fitted for least maximum relative error on [0, 1) (Lawson's
+// iteration of weighted least squares, from the mathematics of 2^f alone),
+// then 2^n applied by v_ldexp_f32.  Relative error below 7.6e-5 over the
+// range the softmax feeds it, far under the 16-bit rounding of P; an x below
+// -149 gives 0.  Six VALU instructions against one v_exp_f32.  Built with
+// -DATTN_EXP2_POLY_EVERY=k, the steady-state softmax takes the second
+// exponential of every k-th packed pair from it; measured slower at every
+// share, so the default build uses none.
+#ifndef ATTN_EXP2_POLY_EVERY
+#define ATTN_EXP2_POLY_EVERY 0
+#endif
+constexpr int kPolyEvery = ATTN_EXP2_POLY_EVERY > 0 ? ATTN_EXP2_POLY_EVERY : 1 << 20;
+__device__ __forceinline__ float exp2_poly(float x) {
+    int n;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(n) : "v"(x));
+    const float f = __builtin_amdgcn_fractf(x);
+    const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(0x1.3f96a4p-4f, f, 0x1.cefc4cp-3f), f,
+                                                  0x1.64444cp-1f), f, 0x1.fff632p-1f);
+    return __builtin_amdgcn_ldexpf(p, n);
+}
+
 template <int DT>
 __device__ __forceinline__ float lo_half(uint32_t u) {
     if constexpr (DT == 0)
@@ -282,7 +305,12 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], f32x16 (&o)[CB],
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * q], c, -m));
-                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * q + 1], c, -m));
+                    const float x1 = __builtin_fmaf(s[kb][r0 + 2 * q + 1], c, -m);
+                    float e1;
+                    if ((4 * ks + q) % kPolyEvery == kPolyEvery - 1)
+                        e1 = exp2_poly(x1);
+                    else
+                        e1 = __builtin_amdgcn_exp2f(x1);
                     const uint32_t pk = pack2<DT>(e0, e1);
                     ph[ks][q] = pk;
                     if constexpr (DT == 0) {
