@@ -34,14 +34,14 @@ struct TileCfg {
 constexpr int kNumConfigs = 5;
 constexpr TileCfg kCfg64[kNumConfigs] = {
     {1, 4, 2, 64, 3},   // 0: 128 rows, 8 waves (two key groups)
-    {1, 8, 1, 64, 3},   // 1: 256 rows, 8 waves
+    {1, 8, 1, 64, 4},   // 1: 256 rows, 8 waves (four stages: one barrier per two tiles)
     {1, 2, 2, 64, 2},   // 2: 64 rows, 4 waves (two key groups), two workgroups per CU
     {1, 1, 1, 64, 3},   // 3: 32 rows, 1 wave (few query rows: decoding)
     {1, 1, 4, 64, 2},   // 4: 32 rows, 4 waves in four key groups (small grids)
 };
 constexpr TileCfg kCfg128[kNumConfigs] = {
     {1, 4, 2, 64, 2},
-    {1, 8, 1, 64, 3},
+    {1, 8, 1, 64, 4},
     {1, 2, 2, 32, 2},
     {1, 1, 1, 32, 3},
     {1, 1, 4, 32, 2},

@@ -31,7 +31,8 @@
 //    is the V^T A-operand layout (8 consecutive keys of one channel per lane).
 //  * K and V tiles are brought to LDS by direct global->LDS loads
 //    (global_load_lds_dwordx4) into an NSTAGE-deep ring: tiles i+1 ..
-//    i+NSTAGE-2 are in flight while tile i is used.  The loop is unrolled
+//    i+NSTAGE-2 are in flight while tile i is used (a four-stage ring
+//    instead loads two tiles at a time and synchronises once per pair).  The loop is unrolled
 //    over the stages and the ring is one K and one V object, so each lane
 //    keeps one LDS address per distinct read and reaches every stage, key
 //    block and key step through the instruction's immediate offset.  The
@@ -379,10 +380,32 @@ struct Kernel {
         pv<EXACT, S>(x, st, ph, pl);
     }
 
+    // With a four-stage ring the workgroup meets once per pair of tiles: at
+    // the even step i both tiles i and i+1 have landed, so a wave that is
+    // ahead runs on into tile i+1 instead of waiting at a barrier, and the
+    // loads of tiles i+2 and i+3 go to the two stages the previous pair held.
+    static constexpr bool PAIR = NSTAGE == 4;
+
     // One pipeline step on ring stage S: wait for tile i, barrier, prefetch
-    // tile i + NSTAGE - 1 into the stage that held tile i - 1, compute tile i.
+    // tile i + NSTAGE - 1 into the stage that held tile i - 1, compute tile i
+    // (with PAIR: the barrier and the loads of two tiles on even steps only).
     template <int S, bool EXACT>
     static __device__ __forceinline__ void step(const Ctx &x, State &st, int i, int my_begin, int my_count) {
+        if constexpr (PAIR) {
+            if constexpr (S % 2 == 0) {
+                // tiles i and i+1 are the only loads in flight: both landed
+                // for every wave, and tiles i-2, i-1 are no longer read
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                block_sync();
+                if (i + 2 < my_count) load_tile(x, my_begin + i + 2, x.kst[(S + 2) % 4], x.vst[(S + 2) % 4]);
+                if (i + 3 < my_count) load_tile(x, my_begin + i + 3, x.kst[(S + 3) % 4], x.vst[(S + 3) % 4]);
+            }
+            if (i < my_count) {
+                const int t = my_begin + i;
+                if (visible_tile(x, t)) compute_tile<EXACT, S>(x, st, t);
+            }
+            return;
+        }
         wait_tiles<LPT>(min(NSTAGE - 2, my_count - 1 - i));
         block_sync();
         constexpr int SN = (S + NSTAGE - 1) % NSTAGE;
@@ -509,10 +532,10 @@ struct Kernel {
         if constexpr (MASK == MASK_WINDOW) min_vis = min(min_vis, p.window);
         const bool exact = min_vis < p.exact_below;
 
-        // ---- prologue: the first NSTAGE-1 tiles in flight, then the main
+        // ---- prologue: the first NSTAGE-1 tiles (two with PAIR) in flight, then the main
         // loop, unrolled over the ring stages; one instance per P mode
 #pragma unroll
-        for (int s = 0; s < NSTAGE - 1; ++s)
+        for (int s = 0; s < (PAIR ? 2 : NSTAGE - 1); ++s)
             if (s < my_count) load_tile(x, my_begin + s, x.kst[s], x.vst[s]);
         if (exact)
             loop<true>(x, st, half, my_begin, my_count);

@@ -25,7 +25,7 @@ hipError_t launch_lockstep_cfg(int cfg, const Params &p, int64_t grid, hipStream
     constexpr bool small = D == 64;
     switch (cfg) {
     case 0: return launch_lockstep_one<D, DT, MASK, 1, 4, 2, 64, small ? 3 : 2, PAGED>(p, grid, stream);
-    case 1: return launch_lockstep_one<D, DT, MASK, 1, 8, 1, 64, 3, PAGED>(p, grid, stream);
+    case 1: return launch_lockstep_one<D, DT, MASK, 1, 8, 1, 64, 4, PAGED>(p, grid, stream);
     case 2: return launch_lockstep_one<D, DT, MASK, 1, 2, 2, small ? 64 : 32, 2, PAGED>(p, grid, stream);
     case 3: return launch_lockstep_one<D, DT, MASK, 1, 1, 1, small ? 64 : 32, 3, PAGED>(p, grid, stream);
     case 4: return launch_lockstep_one<D, DT, MASK, 1, 1, 4, small ? 64 : 32, 2, PAGED>(p, grid, stream);
