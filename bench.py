@@ -296,6 +296,50 @@ def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mi
             "hbm_bytes_per_launch": kf * 1024 * fscale + kw * 1024 * wscale}
 
 
+def torch_naive_time(r, reps: int):
+    """Time the unfused attention the lab verifies and times the kernel against
+    ("Lab 02 - Forward de flash attention en Triton", sections "Bloque C" and
+    "Bloque E"): the full score matrix in the input dtype, a -inf mask,
+    torch.softmax, then P V, on the GPU.  K and V are repeated to the query
+    heads (GQA) and K is transposed into a contiguous copy before timing (a
+    batched 16-bit product whose right operand is a transposed view is not
+    safe on this platform); the mask is built before timing too.  Returns the
+    mean ms per call over `reps` eager calls, and the max-abs difference from
+    the kernel's output."""
+    import torch
+    w = r["w"]
+    G = w.Hq // w.Hkv
+    kk = r["k"].repeat_interleave(G, dim=1) if G > 1 else r["k"]
+    vv = r["v"].repeat_interleave(G, dim=1) if G > 1 else r["v"]
+    kt = kk.transpose(-1, -2).contiguous()
+    vv = vv.contiguous()
+    mask = None
+    if w.causal:
+        ones = torch.ones(w.N, w.N, dtype=torch.bool, device=r["q"].device)
+        mask = ones.triu(1)
+        if w.window > 0:
+            mask = mask | ones.tril(-w.window)
+
+    def naive():
+        s = torch.matmul(r["q"], kt) * w.scale
+        if mask is not None:
+            s = s.masked_fill(mask, float("-inf"))
+        return torch.matmul(torch.softmax(s, dim=-1), vv)
+
+    out = naive()
+    torch.cuda.synchronize()
+    err = float((out.float() - r["o"].float()).abs().max())
+    del out
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        naive()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps, err
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +359,9 @@ def main() -> int:
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="keep the K/V of decoding workloads in pages of this many tokens (random page order) "
                          "and run the paged entry point")
+    ap.add_argument("--vs-torch", action="store_true",
+                    help="also time the unfused PyTorch attention (score matrix, mask, softmax, P V) on the GPU for "
+                         "variants with N <= 8192, and report the kernel's speedup over it")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (attn_bwd) of each variant instead of the forward; "
                          "FLOPs are 2.5x the forward's (the five products of the backward)")
@@ -532,6 +579,12 @@ def main() -> int:
                         "frac_of_hbm": round(r["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
                         "split_kv": r["split"],
                         "plan": r["plan"]})
+        if args.vs_torch and not (r["split"] or r["paged"] or r["bwd"]) and r["w"].N <= 8192:
+            launch(r)                    # the kernel's output, for the difference check
+            torch.cuda.synchronize()
+            tms, err = torch_naive_time(r, reps=max(3, min(50, int(0.5 / max(per_kernel_ms[j] * 1e-3 * 5, 1e-6)))))
+            kernels[-1]["torch_naive"] = {"ms": round(tms, 5), "speedup": round(tms / per_kernel_ms[j], 2),
+                                          "max_abs_diff": err}
 
     result = {
         "metric": ("attention bwd TFLOP/s (10*B*Hq*N^2*d, x1/2 causal) & % of MI355X MFMA peak" if args.backward
