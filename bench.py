@@ -187,6 +187,7 @@ def cpu_baseline_backward(workloads, budget_s: float):
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"fp64 oracle backward (per-row dq entry point) on random query rows of every variant, "
                    f"about {per_variant:.1f} s each ({rows_done} rows, {flops / 1e9:.2f} GFLOP in {elapsed:.1f} s)"),
@@ -229,6 +230,7 @@ def cpu_baseline(workloads, budget_s: float):
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"fp64 oracle on random query rows of every variant, about {per_variant:.1f} s each "
                    f"({rows_done} rows, {flops / 1e9:.2f} GFLOP in {elapsed:.1f} s)"),
@@ -294,6 +296,18 @@ def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mi
             "write_scale": wscale, "hbm_read_bytes": kf * 1024 * fscale,
             "hbm_write_bytes": kw * 1024 * wscale,
             "hbm_bytes_per_launch": kf * 1024 * fscale + kw * 1024 * wscale}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the oracle timing."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def torch_naive_time(r, reps: int):
