@@ -13,9 +13,10 @@
 // Work split: a group of D/4 lanes owns one row, four channels per lane, so
 // each partial-output read is 16 bytes per lane over consecutive channels.
 // `sg` groups share a row and take every sg-th chunk each (the chunk loop is a
-// chain of dependent-latency loads otherwise); each group keeps its own max,
-// weight sum and weighted sum, and the first group of the row combines the sg
-// results through LDS with the same rescale.  The output is rounded to the
+// chain of dependent-latency loads otherwise); each group keeps its own
+// running max, weight sum and weighted sum in one pass over its chunks, and
+// the first group of the row combines the sg results through LDS with the
+// same rescale.  The output is rounded to the
 // 16-bit type once.
 #pragma once
 
@@ -49,24 +50,26 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeParams mp) {
     const int64_t row = (int64_t)blockIdx.x * (G / sg) + rloc;
     const bool live = row < mp.rows;
 
+    // one pass over the group's chunks with a running max: the loads of a
+    // chunk do not wait on the max of the earlier ones, so the unrolled loop
+    // issues them together
     float m = -__builtin_inff();
     float w = 0.0f;
     float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (live) {
 #pragma unroll 8
-        for (int s = part; s < mp.n_splits; s += sg) m = fmaxf(m, mp.ws_ml[s * mp.rows + row]);
-        if (m != -__builtin_inff()) {
-#pragma unroll 8
-            for (int s = part; s < mp.n_splits; s += sg) {
-                const float ls = mp.ws_ml[s * mp.rows + row];
-                const float4 x = *(const float4 *)(mp.ws_o + (s * mp.rows + row) * D + 4 * c4);
-                const float e = (ls == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ls - m);
-                w += e;
-                acc.x += e * x.x;
-                acc.y += e * x.y;
-                acc.z += e * x.z;
-                acc.w += e * x.w;
-            }
+        for (int s = part; s < mp.n_splits; s += sg) {
+            const float ls = mp.ws_ml[s * mp.rows + row];
+            const float4 x = *(const float4 *)(mp.ws_o + (s * mp.rows + row) * D + 4 * c4);
+            const float nm = fmaxf(m, ls);
+            const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - nm);
+            const float e = (ls == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ls - nm);
+            m = nm;
+            w = w * f + e;
+            acc.x = acc.x * f + e * x.x;
+            acc.y = acc.y * f + e * x.y;
+            acc.z = acc.z * f + e * x.z;
+            acc.w = acc.w * f + e * x.w;
         }
     }
     if (c4 == 0) {
