@@ -13,10 +13,28 @@ import oracle
 from attn_inputs import make_qkv, to_bits
 
 # Max-abs tolerances against the fp64 oracle (strict <): output 1e-3 for fp16
-# and 1e-2 for bf16, log-sum-exp 1e-3 for both.
+# and 1e-2 for bf16, log-sum-exp 1e-3 for both.  An output element whose
+# exact value is large enough that one unit in the last place of the 16-bit
+# output type exceeds that bound (|o| >= 2 in fp16 or bf16: a row averaging
+# only a few keys) is held to one such unit instead: even the correctly
+# rounded value can miss 1e-3 there (at |o| in [4, 8) fp16 rounds to steps of
+# 3.9e-3).
 TOL_O = {"f16": 1e-3, "bf16": 1e-2}
 TOL_LSE = 1e-3
 DT_CODE = {"f16": 0, "bf16": 1}
+MANT = {"f16": 10, "bf16": 7}     # explicit mantissa bits of the output type
+
+
+def ulp16(x: np.ndarray, dtype: str) -> np.ndarray:
+    """One unit in the last place of the 16-bit type at |x| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -14)))
+    return 2.0 ** (e - MANT[dtype])
+
+
+def output_bound(o_ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-element output bound: TOL_O, or one 16-bit ulp of the exact value
+    when that is larger."""
+    return np.maximum(TOL_O[dtype], ulp16(o_ref, dtype))
 
 
 def need_gpu():
@@ -113,9 +131,13 @@ def errors(o_gpu, lse_gpu, o_ref, lse_ref):
 
 
 def check(label, o_gpu, lse_gpu, o_ref, lse_ref, dtype):
-    eo, el, _, _ = errors(o_gpu, lse_gpu, o_ref, lse_ref)
+    eo, el, eo_all, _ = errors(o_gpu, lse_gpu, o_ref, lse_ref)
     say(f"  {label}: max|dO| = {eo:.3e} (tol {TOL_O[dtype]:.0e}), max|dLSE| = {el:.3e} (tol {TOL_LSE:.0e})")
-    assert eo < TOL_O[dtype], f"{label}: output error {eo:.3e} >= {TOL_O[dtype]}"
+    if eo_all.size:
+        bound = output_bound(np.asarray(o_ref), dtype)
+        worst = np.unravel_index(np.argmax(eo_all - bound), eo_all.shape)
+        assert (eo_all < bound).all(), (f"{label}: output error {eo_all[worst]:.3e} at {worst} (exact "
+                                        f"{np.asarray(o_ref)[worst]:.6f}) >= {bound[worst]:.3e}")
     assert el < TOL_LSE, f"{label}: lse error {el:.3e} >= {TOL_LSE}"
     return eo, el
 

@@ -11,7 +11,7 @@ import torch
 
 from attn_inputs import WORKLOADS, make_workload
 from gpu_helpers import (DT_CODE, TOL_LSE, TOL_O, check, errors, inputs, need_gpu, oracle_full,
-                         oracle_sampled, run_gpu, sample_rows, say)
+                         oracle_sampled, run_gpu, run_gpu_splitkv, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -251,3 +251,34 @@ def test_plain_random_shapes(fa):
         ro, rl = oracle_full(q, k, v, causal=causal, window=window)
         o, lse = run_gpu(q, k, v, causal=causal, window=window, config_id=cfg)
         check(f"#{n} B{B} Hq{G * Hkv}/{Hkv} N{N} d{d} {dt} c{int(causal)} w{window} cfg{cfg}", o, lse, ro, rl, dt)
+
+
+def test_random_sweep(fa):
+    """A seeded sweep over shapes, head groupings, masks (short windows
+    included, where a row averages a few keys and |o| can pass 2), dtypes,
+    tile configurations and the split-KV entry point with forced chunk
+    counts, against the oracle."""
+    rng = np.random.default_rng(2024)
+    for n in range(80):
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f16", "bf16"]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        N = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 1100)),
+                            int(rng.choice([64, 128, 255, 256, 257, 511, 512, 513, 767, 1024]))]))
+        causal = bool(rng.integers(0, 3) > 0)
+        window = int(rng.choice([0, 0, 1, 2, 31, 64, 65, 127, 300, 1000])) if causal else 0
+        cfgs = list(range(fa.attn_fwd_num_configs()))
+        cfg = int(rng.choice([-1] + cfgs))
+        split = bool(rng.integers(0, 4) == 0)
+        q, k, v = inputs(B, G * Hkv, Hkv, N, d, dt, seed=1000 + n)
+        ro, rl = oracle_full(q, k, v, causal=causal, window=window)
+        label = f"#{n} B{B} Hq{G * Hkv}/{Hkv} N{N} d{d} {dt} c{int(causal)} w{window} cfg{cfg}"
+        if split:
+            nsp = int(rng.choice([0, 2, 3, 7]))
+            o, lse = run_gpu_splitkv(q, k, v, causal=causal, window=window, num_splits=nsp, config_id=cfg)
+            label += f" split-KV {nsp}"
+        else:
+            o, lse = run_gpu(q, k, v, causal=causal, window=window, config_id=cfg)
+        check(label, o, lse, ro, rl, dt)
