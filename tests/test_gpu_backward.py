@@ -205,6 +205,23 @@ def test_bwd_after_hip_forward(fa, case):
     full_case(*case, seed=12, hip_forward=True)
 
 
+# ---- a seeded sweep: shapes, head groupings, dtypes, masks (windows of 1 and 2
+# keys included) and scales (negative and sharp ones included)
+def test_bwd_random_sweep(fa):
+    rng = np.random.default_rng(31)
+    for n in range(40):
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f16", "bf16"]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        N = int(rng.choice([int(rng.integers(1, 130)), int(rng.integers(130, 600))]))
+        causal = bool(rng.integers(0, 3) > 0)
+        window = int(rng.choice([0, 0, 1, 2, 33, 100])) if causal else 0
+        scale = float(rng.choice([1.0 / math.sqrt(d), 1.0 / math.sqrt(d), -0.1, 0.2]))
+        full_case(B, G * Hkv, Hkv, N, d, dt, causal, window, seed=7000 + n, scale=scale)
+
+
 def test_bwd_deterministic(fa):
     q, k, v = make_qkv(1, 8, 2, 500, 128, "bf16", seed=9)
     do = make_dout(1, 8, 500, 128, "bf16", seed=9)

@@ -141,19 +141,19 @@ def test_flash_attn_forward_paged_wrapper(fa):
 def test_paged_random_shapes(fa):
     """Seeded random requests, page sizes, masks, chunk counts and configurations."""
     rng = np.random.default_rng(4321)
-    for n in range(16):
+    for n in range(48):
         d = int(rng.choice([64, 128]))
         dt = str(rng.choice(["f16", "bf16"]))
         Hkv = int(rng.choice([1, 2]))
-        G = int(rng.choice([1, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
         B = int(rng.integers(1, 4))
-        Nq = int(rng.choice([1, 2, 3, 16, 33]))
+        Nq = int(rng.choice([1, 2, 3, 7, 16, 31, 32, 33, 100]))
         lens = [int(x) for x in rng.integers(Nq, 1800, size=B)]
         ps = int(rng.choice([8, 16, 32, 64, 128, 256]))
         causal = bool(rng.integers(0, 4) > 0)
-        window = int(rng.choice([0, 0, 1, 50])) if causal else 0
-        splits = int(rng.choice([0, 1, 3, 40]))
-        cfg = int(rng.choice([-1, 1, 2, 3]))
+        window = int(rng.choice([0, 0, 1, 2, 50, 300])) if causal else 0
+        splits = int(rng.choice([0, 1, 2, 3, 40]))
+        cfg = int(rng.choice([-1, 0, 1, 2, 3, 4]))
         nmax = max(lens)
         q, k, v = make_qkv(B, G * Hkv, Hkv, Nq, d, dt, seed=200 + n, nk=nmax)
         kp, vp, bt, sl = make_paged_cache(k, v, ps, lens, seed=200 + n)
