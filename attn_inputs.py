@@ -120,6 +120,42 @@ def make_dout(B: int, Hq: int, N: int, d: int, dtype: str = "f16", seed: int = 0
     return do.to(TORCH_DTYPES[dtype]).contiguous()
 
 
+SCORE_PATTERNS = ("rising", "slow", "falling", "spikes")
+
+
+def make_score_pattern(pattern: str, N: int, d: int, dtype: str = "f16", seed: int = 0, Hq: int = 2):
+    """Host q (1,Hq,N,d), k and v (1,1,N,d) whose scores follow a set profile
+    along the keys: every channel of q is about 1 and every channel of key j
+    about target_j / sqrt(d), so with scale 1/sqrt(d) score (i, j) is about
+    target_j, plus small noise; v is N(0,1).
+      rising:  target grows by about 7.7 per 64 keys (0 .. 120 over N = 1000);
+      slow:    it grows by about 2.6 per 64 keys (0 .. 40);
+      falling: 120 .. 0, the first keys dominate;
+      spikes:  0, except about 60 at keys 0, 63, 64, 127, 500, 501 and N-1."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    j = torch.arange(N, dtype=torch.float64)
+    if pattern == "rising":
+        target = 120.0 * j / N
+    elif pattern == "slow":
+        target = 40.0 * j / N
+    elif pattern == "falling":
+        target = 120.0 * (N - j) / N
+    elif pattern == "spikes":
+        target = torch.zeros(N, dtype=torch.float64)
+        for s in (0, 63, 64, 127, 500, 501, N - 1):
+            if s < N:
+                target[s] = 60.0
+    else:
+        raise ValueError(f"unknown score pattern {pattern!r}")
+    tdt = TORCH_DTYPES[dtype]
+    q = (1.0 + 0.05 * torch.randn(1, Hq, N, d, generator=g, dtype=torch.float64)).to(tdt)
+    k = (target[None, None, :, None] / math.sqrt(d)
+         + 0.05 * torch.randn(1, 1, N, d, generator=g, dtype=torch.float64)).to(tdt)
+    v = torch.randn(1, 1, N, d, generator=g, dtype=torch.float64).to(tdt)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
 def make_paged_cache(k: torch.Tensor, v: torch.Tensor, page_size: int, seq_lens, seed: int = 0,
                      spare_pages: int = 3):
     """Scatter contiguous host K/V (B, Hkv, Nmax, d) into page pools

@@ -53,7 +53,8 @@ def model_bwd(q, k, v, do, o, lse, *, scale: float, causal: bool, window: int, d
     if window:
         vis &= (i - j) < window
     c2 = np.float32(float(s32) * LOG2E)
-    P = np.where(vis, np.exp2(S * c2 - L[..., None] * np.float32(LOG2E)), 0.0).astype(np.float32)
+    with np.errstate(over="ignore"):           # masked scores may overflow; they are dropped
+        P = np.where(vis, np.exp2(S * c2 - L[..., None] * np.float32(LOG2E)), 0.0).astype(np.float32)
     dP = np.matmul(dof, np.swapaxes(vv, -1, -2)).astype(np.float32)
     D = (dof * O).sum(-1, dtype=np.float32)
     dS = (P * (dP - D[..., None])).astype(np.float32)

@@ -25,7 +25,7 @@ import pytest
 import torch
 
 import oracle
-from attn_inputs import make_dout, make_qkv, to_bits
+from attn_inputs import SCORE_PATTERNS, make_dout, make_qkv, make_score_pattern, to_bits
 from bwd_rounding_model import model_bwd, oracle_forward_inputs
 from gpu_helpers import DT_CODE, need_gpu, say
 
@@ -82,7 +82,12 @@ def run_bwd(q, k, v, do, *, causal, window=0, scale=None, poison=True, o=None, l
 # 7.5 u at the default scale 1/sqrt(d) with no window or one of 64 keys or
 # more.  So where the whole tensors are checked, and the model and the kernels
 # receive the same O and lse, a slice's bound is twice the model's own error
-# on that slice plus MODEL_SLACK u of the slice's scale.  The fixed multiples
+# on that slice plus MODEL_SLACK u of the slice's scale.  Where nearly every
+# row's P is one-hot and the keys are long and alike (the score profiles of
+# make_score_pattern), dq is mostly rounding of dS: the model's median row is
+# 4-38 u and its worst 33-350 u, and the rows that carry the most noise differ
+# between the model and the kernels; there (median above MODEL_SLACK u) every
+# slice may reach twice the model's worst slice.  The fixed multiples
 # hold the cases that take the HIP forward's O: at the default scale with no
 # short window.  (The forward rounds P before P.V, so its O differs from the
 # correctly rounded one in a few last bits; through D = rowsum(dO * O) that
@@ -110,7 +115,15 @@ def check_slices(label, name, g, r, dtype, m=None):
     if m is None:
         bound = mult * u * ref
     else:
-        bound = 2 * np.abs(m - r).max(axis=-1) + MODEL_SLACK * u * ref
+        merr = np.abs(m - r).max(axis=-1)
+        bound = 2 * merr + MODEL_SLACK * u * ref
+        # slices that are mostly rounding noise (the model's median slice error
+        # above MODEL_SLACK u): which of them carry the most noise differs
+        # between the model and the kernels, so each may reach twice the
+        # model's worst slice
+        rel = merr / ref
+        if np.median(rel) > MODEL_SLACK * u:
+            bound = np.maximum(bound, 2 * rel.max() * ref)
     bad = np.flatnonzero(err >= bound)
     worst = float((err / ref).max() / u)
     if bad.size:
@@ -122,6 +135,10 @@ def check_slices(label, name, g, r, dtype, m=None):
 
 
 def check_grads(label, got, ref, dtype, model=None):
+    """Tensor-wide and per-slice bounds.  With the rounding model's values,
+    the tensor-wide bound is also at least twice the model's own error: where
+    every row's P is nearly one-hot and the keys are long and alike, dq is a
+    small difference of large terms and the rounding of dS dominates it."""
     worst, slices = [], []
     for t, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), got, ref)):
         gd = g.to(torch.float64).numpy().reshape(r.shape)
@@ -130,7 +147,10 @@ def check_grads(label, got, ref, dtype, model=None):
         err = float(np.abs(gd - r).max()) if r.size else 0.0
         rel = err / scale if scale > 0 else err
         worst.append(rel)
-        assert rel < TOL_BWD[dtype], f"{label}: {name} error {err:.3e} = {rel:.2e} x max|ref| >= {TOL_BWD[dtype]:.2e}"
+        tol = TOL_BWD[dtype]
+        if model is not None and scale > 0:
+            tol = max(tol, 2 * float(np.abs(model[t] - r).max()) / scale)
+        assert rel < tol, f"{label}: {name} error {err:.3e} = {rel:.2e} x max|ref| >= {tol:.2e}"
         d = r.shape[-1] if r.ndim else 1
         m = None if model is None else model[t].reshape(-1, d)
         slices.append(check_slices(label, name, gd.reshape(-1, d), np.asarray(r).reshape(-1, d), dtype, m))
@@ -145,6 +165,13 @@ def full_case(B, Hq, Hkv, N, d, dtype, causal, window=0, seed=0, scale=None, hip
     label = f"bwd B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} W={window} seed={seed}"
     if scale is not None:
         label += f" scale={scale}"
+    return check_case(label, q, k, v, do, dtype, causal, window, scale, hip_forward)
+
+
+def check_case(label, q, k, v, do, dtype, causal, window=0, scale=None, hip_forward=False):
+    """Whole tensors of the HIP backward against the oracle (and, unless the
+    HIP forward's o and lse are used, the rounding model's slice bounds)."""
+    d = q.shape[-1]
     if hip_forward:
         label += " (HIP forward's o, lse)"
     say(f"case {label}")
@@ -220,6 +247,19 @@ def test_bwd_random_sweep(fa):
         window = int(rng.choice([0, 0, 1, 2, 33, 100])) if causal else 0
         scale = float(rng.choice([1.0 / math.sqrt(d), 1.0 / math.sqrt(d), -0.1, 0.2]))
         full_case(B, G * Hkv, Hkv, N, d, dt, causal, window, seed=7000 + n, scale=scale)
+
+
+# ---- the score profiles that drive the forward's online softmax (a running max
+# raised on every tile, a stale one, underflow, spikes at tile edges): here they
+# give rows whose P is nearly one-hot, where dS cancels hardest
+@pytest.mark.parametrize("pattern", SCORE_PATTERNS)
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
+def test_bwd_score_patterns(fa, pattern, d, dtype):
+    N = 500
+    for n_case, causal in enumerate((False, True)):
+        q, k, v = make_score_pattern(pattern, N, d, dtype, seed=23 + n_case)
+        do = make_dout(1, q.shape[1], N, d, dtype, seed=23 + n_case)
+        check_case(f"bwd score pattern {pattern} N{N} d{d} {dtype} causal={causal}", q, k, v, do, dtype, causal)
 
 
 def test_bwd_deterministic(fa):

@@ -3,14 +3,13 @@ same seeded inputs, element by element, with the stated tolerances."""
 from __future__ import annotations
 
 import json
-import math
 import os
 
 import numpy as np
 import pytest
 import torch
 
-from attn_inputs import WORKLOADS, make_workload
+from attn_inputs import SCORE_PATTERNS, WORKLOADS, make_score_pattern, make_workload
 from gpu_helpers import (DT_CODE, TOL_LSE, TOL_O, check, errors, inputs, need_gpu, oracle_full,
                          oracle_sampled, run_gpu, run_gpu_splitkv, sample_rows, say)
 
@@ -287,46 +286,21 @@ def test_random_sweep(fa):
 
 # ---- inputs built to drive the online softmax's own logic ("Optimizaciones de
 # Atencion", section "FlashAttention: Nunca materializar la matriz de atencion":
-# the running max and the rescale of the sum and accumulator when it grows).
-# Scores s_ij ~ target_j: every channel of q is about 1 and every channel of
-# key j about target_j / sqrt(d), so with scale 1/sqrt(d) the score is about
-# target_j (plus small noise).
-#   rising: target grows by ~7.7 (about 11 in base 2) per 64-key tile, so the
-#           running max is raised on nearly every tile;
-#   slow:   it grows by ~2.6 per tile, below the raise threshold, so tiles are
-#           accepted against a stale max until the growth adds up;
-#   falling: the first keys dominate and later tiles underflow to zero;
-#   spikes: a few keys on both sides of tile edges sit ~60 above the rest.
-def softmax_stress_inputs(pattern, N, d, dtype, seed):
-    g = torch.Generator().manual_seed(seed)
-    j = torch.arange(N, dtype=torch.float64)
-    if pattern == "rising":
-        target = 120.0 * j / N
-    elif pattern == "slow":
-        target = 40.0 * j / N
-    elif pattern == "falling":
-        target = 120.0 * (N - j) / N
-    else:
-        target = torch.zeros(N, dtype=torch.float64)
-        for s in (0, 63, 64, 127, 500, 501, N - 1):
-            target[s] = 60.0
-    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
-    q = (1.0 + 0.05 * torch.randn(1, 2, N, d, generator=g, dtype=torch.float64)).to(tdt)
-    k = (target[None, None, :, None] / math.sqrt(d)
-         + 0.05 * torch.randn(1, 1, N, d, generator=g, dtype=torch.float64)).to(tdt)
-    v = torch.randn(1, 1, N, d, generator=g, dtype=torch.float64).to(tdt)
-    return q, k, v
-
-
-@pytest.mark.parametrize("pattern", ["rising", "slow", "falling", "spikes"])
+# the running max and the rescale of the sum and accumulator when it grows;
+# make_score_pattern gives the profiles): rising raises the running max on
+# nearly every 64-key tile; slow grows below the raise threshold, so tiles are
+# accepted against a stale max until the growth adds up; falling lets later
+# tiles underflow to zero; spikes put a few dominant keys on both sides of tile
+# edges.
+@pytest.mark.parametrize("pattern", SCORE_PATTERNS)
 @pytest.mark.parametrize("d,dtype", [(64, "f16"), (64, "bf16"), (128, "bf16"), (128, "f16")])
 def test_softmax_stress_patterns(fa, pattern, d, dtype):
     N = 1000
     for n_case, causal in enumerate((False, True)):
-        forced = (["rising", "slow", "falling", "spikes"].index(pattern) + d // 64 + 2 * n_case
+        forced = (SCORE_PATTERNS.index(pattern) + d // 64 + 2 * n_case
                   + (dtype == "bf16")) % fa.attn_fwd_num_configs()
         for cfg in (-1, forced):
-            q, k, v = softmax_stress_inputs(pattern, N, d, dtype, seed=17 + n_case)
+            q, k, v = make_score_pattern(pattern, N, d, dtype, seed=17 + n_case)
             ro, rl = oracle_full(q, k, v, causal=causal)
             o, lse = run_gpu(q, k, v, causal=causal, config_id=cfg)
             check(f"softmax stress {pattern} d{d} {dtype} causal={causal} cfg{cfg}", o, lse, ro, rl, dtype)
