@@ -10,9 +10,11 @@ forward.  Tolerance, per output tensor X in {dq, dk, dv}: max|X_gpu - X_ref|
 2^-8 bf16).  The kernels round P and dS to that type as MFMA operands and
 round the outputs once; a numpy model of exactly that scheme
 (bwd_rounding_model) against the same oracle stays below 1.6 u on every case
-here, so 4 u leaves a margin of more than 2 while any error in a term (a
-wrong mask, scale, head map or transposed operand) shows up at the size of
-the gradient itself.  Each row of dq and each key's row of dk and dv is also
+with random inputs here, so 4 u leaves a margin of more than 2 while any
+error in a term (a wrong mask, scale, head map or transposed operand) shows
+up at the size of the gradient itself.  On the score profiles with nearly
+one-hot P the model's own dq error is far larger, and the bound follows it
+(check_grads).  Each row of dq and each key's row of dk and dv is also
 held to a bound of its own (check_slices below), so that an error confined
 to rows with small gradients shows up too.
 """
