@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from attn_inputs import WORKLOADS, make_qkv, make_workload
+from attn_inputs import SCORE_PATTERNS, WORKLOADS, make_qkv, make_score_pattern, make_workload
 from gpu_helpers import (TOL_LSE, TOL_O, check, need_gpu, oracle_full, oracle_sampled, run_gpu,
                          run_gpu_splitkv, sample_rows, say)
 
@@ -170,3 +170,22 @@ def test_splitkv_random_shapes(fa):
         o, lse = run_gpu_splitkv(q, k, v, causal=causal, window=window, num_splits=splits, config_id=cfg)
         check(f"#{n} B{B} Hq{G * Hkv}/{Hkv} Nq{Nq} Nk{Nk} d{d} {dt} c{int(causal)} w{window} s{splits} cfg{cfg}",
               o, lse, ro, rl, dt)
+
+
+# ---- the score profiles of make_score_pattern: with scores rising by 120
+# along the keys the later chunks outweigh the earlier ones by about e^120,
+# with falling scores the reverse, and spikes sit on chunk edges; the merge's
+# rescale ("Optimizaciones de Atencion", section "FlashDecoding") must take
+# partial results whose maxima differ that much.  Decoding (4 new rows, two
+# query heads stacked on one K/V head) and square shapes.
+@pytest.mark.parametrize("pattern", SCORE_PATTERNS)
+@pytest.mark.parametrize("d,dt", [(64, "f16"), (128, "bf16")])
+def test_splitkv_score_patterns(fa, pattern, d, dt):
+    N = 1000
+    q, k, v = make_score_pattern(pattern, N, d, dt, seed=31)
+    for nq in (4, N):
+        qq = q[:, :, N - nq:].contiguous()
+        ro, rl = oracle_full(qq, k, v, causal=True)
+        for cfg, splits in ((-1, 0), (-1, 2), (-1, 7), (3, 40), (0, 5)):
+            o, lse = run_gpu_splitkv(qq, k, v, causal=True, num_splits=splits, config_id=cfg)
+            check(f"split-KV {pattern} Nq{nq} Nk{N} d{d} {dt} cfg{cfg} splits{splits}", o, lse, ro, rl, dt)
