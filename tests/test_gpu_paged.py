@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from attn_inputs import WORKLOADS, make_paged_cache, make_qkv, make_workload, to_bits
+from attn_inputs import SCORE_PATTERNS, WORKLOADS, make_paged_cache, make_qkv, make_score_pattern, make_workload, to_bits
 from gpu_helpers import DT_CODE, check, need_gpu, run_gpu_splitkv, say
 
 pytestmark = pytest.mark.gpu
@@ -162,3 +162,19 @@ def test_paged_random_shapes(fa):
                                num_splits=splits, config_id=cfg)
         check(f"#{n} B{B} Hq{G * Hkv}/{Hkv} Nq{Nq} lens{lens} ps{ps} d{d} {dt} c{int(causal)} w{window} "
               f"s{splits} cfg{cfg}", o, lse, ro, rl, dt)
+
+
+# ---- the score profiles of make_score_pattern behind a block table (pages in
+# seeded random order): chunk maxima that differ by up to e^120 and spikes on
+# page and chunk edges, for decoding rows against one request of 1000 keys
+@pytest.mark.parametrize("pattern", SCORE_PATTERNS)
+@pytest.mark.parametrize("d,dt", [(64, "f16"), (128, "bf16")])
+def test_paged_score_patterns(fa, pattern, d, dt):
+    N = 1000
+    q, k, v = make_score_pattern(pattern, N, d, dt, seed=37)
+    qq = q[:, :, N - 4:].contiguous()
+    for ps, splits in ((16, 0), (64, 7), (256, 2)):
+        kp, vp, bt, sl = make_paged_cache(k, v, ps, [N], seed=37 + ps)
+        ro, rl = oracle_paged(qq, kp, vp, bt, sl, causal=True)
+        o, lse = run_gpu_paged(qq, kp, vp, bt, sl, max_seq_len=bt.shape[1] * ps, causal=True, num_splits=splits)
+        check(f"paged {pattern} ps{ps} splits{splits} d{d} {dt}", o, lse, ro, rl, dt)
