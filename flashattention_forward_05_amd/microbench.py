@@ -144,6 +144,13 @@ def measure(quick: bool = False) -> dict:
     out["overlap_mfma_with_exp"] = pair(K_MFMA32, 4000, K_EXP, 8000)
     out["overlap_mfma_with_fma"] = pair(K_MFMA32, 4000, K_FMA, 32000)
     out["overlap_exp_with_fma"] = pair(K_EXP, 8000, K_FMA, 32000)
+    # waves that mix kinds, as the attention kernels' waves do: an MFMA chain
+    # whose operands come from LDS, or with vector work between the MFMAs,
+    # beside a wave of exponentials or of the same mix
+    out["overlap_mfma_lds_with_exp"] = pair(K_MFMA_LDS, 4000, K_EXP, 8000)
+    out["overlap_mfma_fma4_with_exp"] = pair(K_MFMA_FMA4, 4000, K_EXP, 8000)
+    out["overlap_mfma_exp2_with_mfma_exp2"] = pair(K_MFMA_EXP2, 4000, K_MFMA_EXP2, 4000)
+    out["overlap_mfma_with_mfma_exp2"] = pair(K_MFMA32, 4000, K_MFMA_EXP2, 4000)
 
     ms, t, r, _, _ = _run(K_LDS, K_LDS, it_v, it_v)
     out["lds_read_b128_bytes_per_clk_cu"] = _per_cu_clk(K_LDS, it_v, t, list(range(8)))
