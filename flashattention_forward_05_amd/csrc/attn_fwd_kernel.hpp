@@ -91,6 +91,7 @@ struct Kernel {
         const uint16_t *kp, *vp;
         int Nq, Nk, window, lane, g, l32, wave_q, kgroup;
         int qw0, pw0, w_last, q_off;
+        bool loader;   // LOADERS: this wave issues its partner's loads as well
         int lpos[QB];
         // paged K/V: this batch's block-table row, the K/V head and the page geometry
         const int32_t *bt;
@@ -190,6 +191,44 @@ struct Kernel {
     // stage; slot i is at + i * NWQ * 1024.
     static __device__ __forceinline__ uint32_t lds_base(const Ctx &x, const char *stage) {
         return __builtin_amdgcn_readfirstlane(lds_addr(stage + x.kgroup * TILEB + x.wave_q * 1024));
+    }
+
+    // Contiguous K/V: tile t into the load slots of query wave wq of this
+    // wave's key group.
+    static __device__ __forceinline__ void load_tile_as(const Ctx &x, int t, char *kdst, char *vdst, int wq) {
+        const int j0 = t * BN;
+        const uint32_t kb = __builtin_amdgcn_readfirstlane(lds_addr(kdst + x.kgroup * TILEB + wq * 1024));
+        const uint32_t vb = __builtin_amdgcn_readfirstlane(lds_addr(vdst + x.kgroup * TILEB + wq * 1024));
+        static_for<LOADS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int slot = (i * NWQ + wq) * 64 + x.lane;
+            const int row = slot / CHUNKS_PER_ROW;
+            const int chp = slot % CHUNKS_PER_ROW;
+            const int ch = chp ^ swz<D>(row);
+            const int64_t grow = min(j0 + row, x.Nk - 1);
+            const int64_t off = grow * D + ch * 8;
+            lds_dma16_at<i * NWQ * 1024>(x.kp + off, kb);
+            lds_dma16_at<i * NWQ * 1024>(x.vp + off, vb);
+        });
+    }
+
+    // The 256-row configuration (eight query waves on one key range, waves w
+    // and w + 4 on one SIMD): the waves w + 4 lose the SIMD's issue to the
+    // waves w and set the pace, while the waves w wait at the barrier.  So
+    // waves 0-3 issue every tile load, their own slots and those of wave w + 4,
+    // right after the barrier, and waves 4-7 issue none.
+    static constexpr bool LOADERS = !PAGED && KSPLIT == 1 && NWQ == 8 && NSTAGE == 4;
+
+    // Tile t into this wave's load slots (and, for a loader, its partner's).
+    static __device__ __forceinline__ void load_tile_step(const Ctx &x, int t, char *kdst, char *vdst) {
+        if constexpr (LOADERS) {
+            if (x.loader) {
+                load_tile_as(x, t, kdst, vdst, x.wave_q);
+                load_tile_as(x, t, kdst, vdst, x.wave_q + NWQ / 2);
+            }
+        } else {
+            load_tile(x, t, kdst, vdst);
+        }
     }
 
     static __device__ __forceinline__ void load_tile(const Ctx &x, int t, char *kdst, char *vdst) {
@@ -397,8 +436,8 @@ struct Kernel {
                 // for every wave, and tiles i-2, i-1 are no longer read
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 block_sync();
-                if (i + 2 < my_count) load_tile(x, my_begin + i + 2, x.kst[(S + 2) % 4], x.vst[(S + 2) % 4]);
-                if (i + 3 < my_count) load_tile(x, my_begin + i + 3, x.kst[(S + 3) % 4], x.vst[(S + 3) % 4]);
+                if (i + 2 < my_count) load_tile_step(x, my_begin + i + 2, x.kst[(S + 2) % 4], x.vst[(S + 2) % 4]);
+                if (i + 3 < my_count) load_tile_step(x, my_begin + i + 3, x.kst[(S + 3) % 4], x.vst[(S + 3) % 4]);
             }
             if (i < my_count) {
                 const int t = my_begin + i;
@@ -534,9 +573,10 @@ struct Kernel {
 
         // ---- prologue: the first NSTAGE-1 tiles (two with PAIR) in flight, then the main
         // loop, unrolled over the ring stages; one instance per P mode
+        x.loader = x.wave_q < NWQ / 2;
 #pragma unroll
         for (int s = 0; s < (PAIR ? 2 : NSTAGE - 1); ++s)
-            if (s < my_count) load_tile(x, my_begin + s, x.kst[s], x.vst[s]);
+            if (s < my_count) load_tile_step(x, my_begin + s, x.kst[s], x.vst[s]);
         if (exact)
             loop<true>(x, st, half, my_begin, my_count);
         else
