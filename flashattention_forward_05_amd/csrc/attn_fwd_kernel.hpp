@@ -30,7 +30,8 @@
 //    16-lane group, column j of the 4 x 16 block the group addressed, which
 //    is the V^T A-operand layout (8 consecutive keys of one channel per lane).
 //  * K and V tiles are brought to LDS by direct global->LDS loads
-//    (global_load_lds_dwordx4) into an NSTAGE-deep ring: tiles i+1 ..
+//    (global_load_lds_dwordx4; with eight waves, issued by waves 0-3 alone,
+//    see LOADERS) into an NSTAGE-deep ring: tiles i+1 ..
 //    i+NSTAGE-2 are in flight while tile i is used (a four-stage ring
 //    instead loads two tiles at a time and synchronises once per pair).  The loop is unrolled
 //    over the stages and the ring is one K and one V object, so each lane
@@ -212,12 +213,15 @@ struct Kernel {
         });
     }
 
-    // The 256-row configuration (eight query waves on one key range, waves w
-    // and w + 4 on one SIMD): the waves w + 4 lose the SIMD's issue to the
-    // waves w and set the pace, while the waves w wait at the barrier.  So
-    // waves 0-3 issue every tile load, their own slots and those of wave w + 4,
-    // right after the barrier, and waves 4-7 issue none.
-    static constexpr bool LOADERS = !PAGED && KSPLIT == 1 && NWQ == 8 && NSTAGE == 4;
+    // Eight-wave configurations (waves w and w + 4 on one SIMD): the waves
+    // w + 4 lose the SIMD's issue to the waves w and set the pace, while the
+    // waves w wait at the barrier.  So waves 0-3 issue every tile load, their
+    // own slots and those of wave w + 4, right after the barrier, and waves
+    // 4-7 issue none.
+    // With two key groups (the 128-row configuration) the waves are numbered
+    // group-minor (key group = wave % 2) so that waves w and w + 4 share a key
+    // group, and the same scheme applies.
+    static constexpr bool LOADERS = !PAGED && NWQ * KSPLIT == 8 && (KSPLIT == 1 || KSPLIT == 2);
 
     // Tile t into this wave's load slots (and, for a loader, its partner's).
     static __device__ __forceinline__ void load_tile_step(const Ctx &x, int t, char *kdst, char *vdst) {
@@ -445,10 +449,11 @@ struct Kernel {
             }
             return;
         }
-        wait_tiles<LPT>(min(NSTAGE - 2, my_count - 1 - i));
+        // a loader issues the loads of two waves per tile
+        wait_tiles<(LOADERS ? 2 : 1) * LPT>(min(NSTAGE - 2, my_count - 1 - i));
         block_sync();
         constexpr int SN = (S + NSTAGE - 1) % NSTAGE;
-        if (i + NSTAGE - 1 < my_count) load_tile(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
+        if (i + NSTAGE - 1 < my_count) load_tile_step(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
         if (i < my_count) {
             const int t = my_begin + i;
             if (visible_tile(x, t)) compute_tile<EXACT, S>(x, st, t);
@@ -472,8 +477,8 @@ struct Kernel {
         Ctx x;
         x.lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        x.wave_q = wave % NWQ;
-        x.kgroup = wave / NWQ;
+        x.wave_q = (LOADERS && KSPLIT == 2) ? wave / 2 : wave % NWQ;
+        x.kgroup = (LOADERS && KSPLIT == 2) ? wave % 2 : wave / NWQ;
         x.g = x.lane >> 5;
         x.l32 = x.lane & 31;
         x.Nq = p.N;
