@@ -85,13 +85,17 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int ca
 // workgroups; larger unmasked grids keep the 128-row workgroups (0).  When
 // even 32-row workgroups are at most one per compute unit, 32 rows with four
 // key groups (4) keep every SIMD busy.
-int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask) {
+int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask, bool pairs = true) {
     const int64_t wg128 = B * Hq * ((N + 127) / 128);
     if (d == 128) {
         const int64_t wg256 = B * Hq * ((N + 255) / 256);
         return wg256 >= 512 ? 1 : 0;
     }
     if (B * Hq * ((N + 31) / 32) <= 256) return 4;
+    // causal: configuration 0 runs paired 64-row tiles of equal work (where the
+    // launch can pair them: not for paged K/V or stacked heads); below about one
+    // workgroup per compute unit the 64-row workgroups fill more units
+    if (mask == attnfwd::MASK_CAUSAL && pairs) return wg128 >= 128 ? 0 : 2;
     if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 2 : 0;
     return wg128 < 128 ? 2 : 0;
 }
@@ -229,10 +233,10 @@ KvView kv_view(int64_t Hq, int64_t Hkv, int64_t Nq) {
 // more loads in flight per compute unit; longer query blocks take the choice
 // of the plain forward, with 64-row workgroups (2) in place of the four-key-
 // group ones (4): key chunks already spread a small grid.
-int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask) {
+int splitkv_auto_config(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int mask, bool pairs) {
     if (Nq < 32) return 3;
     if (Nq <= 128) return 0;
-    const int id = auto_config(B, Hq, Nq, d, mask);
+    const int id = auto_config(B, Hq, Nq, d, mask, pairs);
     return id == 4 ? 2 : id;
 }
 
@@ -380,8 +384,10 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
 
     const int mask = mask_mode(causal, window);
     Params p = make_params(q, k, v, o, lse, B, Hq, Hkv, N, N, window, mask, scale, ntiles);
-    // two 64-row workgroups share a compute unit: pair heavy and light tiles
-    p.zigzag = (id == 2) ? 1 : 0;
+    // two 64-row workgroups share a compute unit: pair heavy and light tiles;
+    // causal, 128 rows: two 64-row tiles of equal combined work per workgroup
+    // (ceil(ceil(N / 64) / 2) = ceil(N / 128) pairs: the grid is the same)
+    p.zigzag = (id == 2) ? 1 : (id == 0 && mask == attnfwd::MASK_CAUSAL) ? 2 : 0;
     const hipError_t err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
     return status_of(err);
 }
@@ -403,7 +409,7 @@ int attn_fwd_splitkv_validate(const void *q, const void *k, const void *v, const
     if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
     const KvView kv = kv_view(Hq, Hkv, Nq);
-    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window), kv.pack_nq == 0);
     const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)workspace;
     if ((mis & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_ALIGN;
     if (Nq == 0) return ATTN_OK;
@@ -440,7 +446,7 @@ int attn_fwd_splitkv_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_
     if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
     const KvView kv = kv_view(Hq, Hkv, Nq);
-    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window), kv.pack_nq == 0);
     const TileCfg &tc = tile_cfg(d, id);
     const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, Nk, Nk - Nq, causal, window, d, num_splits, id);
     if (plan) {
@@ -476,14 +482,14 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
     if (Nq == 0) return ATTN_OK;
     const int mask = mask_mode(causal, window);
     const KvView kv = kv_view(Hq, Hkv, Nq);
-    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask, kv.pack_nq == 0);
     const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, Nk, Nk - Nq, causal, window, d, num_splits, id);
     // stacked heads: B * Hkv heads of G * Nq rows, each its own K/V head
     Params p = make_params(q, k, v, o, lse, B, kv.Hq, kv.pack_nq > 0 ? kv.Hq : Hkv, kv.Nq, Nk, window, mask,
                            scale, sp.ntiles);
     p.q_off = (int)(Nk - Nq);
     p.pack_nq = kv.pack_nq;
-    p.zigzag = (id == 2) ? 1 : 0;
+    p.zigzag = (id == 2) ? 1 : (id == 0 && mask == attnfwd::MASK_CAUSAL && kv.pack_nq == 0) ? 2 : 0;
     p.n_splits = (int)sp.n_splits;
     p.split_tiles = (int)sp.split_tiles;
     p.split_t0 = (int)sp.t0;
@@ -633,7 +639,7 @@ int attn_fwd_paged_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
     if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
     if (config_id < -1 || config_id >= kNumConfigs) return ATTN_ERR_ARG;
     const KvView kv = kv_view(Hq, Hkv, Nq);
-    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window));
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask_mode(causal, window), false);
     const TileCfg &tc = tile_cfg(d, id);
     // lengths differ per batch: chunks cover [0, max_seq_len)
     const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, max_seq_len, 0, 0, 0, d, num_splits, id);
@@ -718,7 +724,7 @@ int attn_fwd_paged_ex(const void *q, const void *k_pool, const void *v_pool, con
     if (Nq == 0) return ATTN_OK;
     const int mask = mask_mode(causal, window);
     const KvView kv = kv_view(Hq, Hkv, Nq);
-    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask);
+    const int id = config_id >= 0 ? config_id : splitkv_auto_config(B, kv.Hq, kv.Nq, d, mask, false);
     const SplitPlan sp = plan_split(B, kv.Hq, kv.Nq, max_seq_len, 0, 0, 0, d, num_splits, id);
     Params p = make_params(q, k_pool, v_pool, o, lse, B, kv.Hq, kv.pack_nq > 0 ? kv.Hq : Hkv, kv.Nq, max_seq_len,
                            window, mask, scale, sp.ntiles);

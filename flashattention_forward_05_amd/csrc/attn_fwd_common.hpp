@@ -64,7 +64,9 @@ struct Params {
     int xcd_kv;          // 1 = place all query heads of a K/V head on one XCD (see bh_of)
     int zigzag;          // masked runs: 1 = ranks 0 .. n/2-1 take the tiles heavy-first and the
                          // rest light-first (pairs a heavy and a light tile per compute unit
-                         // when two workgroups share one), 0 = heavy-first throughout
+                         // when two workgroups share one), 0 = heavy-first throughout;
+                         // 2 = (128-row configuration, causal) the workgroup of rank r takes
+                         // the 64-row query tiles r and ceil(N/64) - 1 - r (equal work)
     float c;             // |scale| * log2(e), at least 2^-100
     uint32_t qsign;      // 0x80008000 when scale < 0 (flips the sign of Q), else 0
 };

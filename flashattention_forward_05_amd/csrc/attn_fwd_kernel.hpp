@@ -92,6 +92,7 @@ struct Kernel {
         const uint16_t *kp, *vp;
         int Nq, Nk, window, lane, g, l32, wave_q, kgroup;
         int qw0, pw0, w_last, q_off;
+        int tstride;             // key tiles of one group: my_begin + i * tstride
         bool loader;   // LOADERS: this wave issues its partner's loads as well
         int lpos[QB];
         // paged K/V: this batch's block-table row, the K/V head and the page geometry
@@ -429,6 +430,15 @@ struct Kernel {
     // loads of tiles i+2 and i+3 go to the two stages the previous pair held.
     static constexpr bool PAIR = NSTAGE == 4;
 
+    // Paired 64-row query tiles (causal, 128-row configuration): the key
+    // groups take alternate tiles, so the few tiles of the light rows are
+    // shared by both groups.
+    static constexpr bool PAIRABLE = MASK == MASK_CAUSAL && !PAGED && NWQ == 4 && KSPLIT == 2 && QB == 1;
+    static __device__ __forceinline__ int tile_at(const Ctx &x, int my_begin, int i) {
+        if constexpr (PAIRABLE) return my_begin + i * x.tstride;
+        return my_begin + i;
+    }
+
     // One pipeline step on ring stage S: wait for tile i, barrier, prefetch
     // tile i + NSTAGE - 1 into the stage that held tile i - 1, compute tile i
     // (with PAIR: the barrier and the loads of two tiles on even steps only).
@@ -440,11 +450,11 @@ struct Kernel {
                 // for every wave, and tiles i-2, i-1 are no longer read
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 block_sync();
-                if (i + 2 < my_count) load_tile_step(x, my_begin + i + 2, x.kst[(S + 2) % 4], x.vst[(S + 2) % 4]);
-                if (i + 3 < my_count) load_tile_step(x, my_begin + i + 3, x.kst[(S + 3) % 4], x.vst[(S + 3) % 4]);
+                if (i + 2 < my_count) load_tile_step(x, tile_at(x, my_begin, i + 2), x.kst[(S + 2) % 4], x.vst[(S + 2) % 4]);
+                if (i + 3 < my_count) load_tile_step(x, tile_at(x, my_begin, i + 3), x.kst[(S + 3) % 4], x.vst[(S + 3) % 4]);
             }
             if (i < my_count) {
-                const int t = my_begin + i;
+                const int t = tile_at(x, my_begin, i);
                 if (visible_tile(x, t)) compute_tile<EXACT, S>(x, st, t);
             }
             return;
@@ -453,9 +463,9 @@ struct Kernel {
         wait_tiles<(LOADERS ? 2 : 1) * LPT>(min(NSTAGE - 2, my_count - 1 - i));
         block_sync();
         constexpr int SN = (S + NSTAGE - 1) % NSTAGE;
-        if (i + NSTAGE - 1 < my_count) load_tile_step(x, my_begin + i + NSTAGE - 1, x.kst[SN], x.vst[SN]);
+        if (i + NSTAGE - 1 < my_count) load_tile_step(x, tile_at(x, my_begin, i + NSTAGE - 1), x.kst[SN], x.vst[SN]);
         if (i < my_count) {
-            const int t = my_begin + i;
+            const int t = tile_at(x, my_begin, i);
             if (visible_tile(x, t)) compute_tile<EXACT, S>(x, st, t);
         }
     }
@@ -528,6 +538,20 @@ struct Kernel {
 
         const int q_tile0 = qt * BM;
         x.qw0 = q_tile0 + x.wave_q * QB * 32;
+        int row_lo = q_tile0, row_hi = min(q_tile0 + BM, N) - 1;
+        if constexpr (MASK == MASK_CAUSAL && !PAGED && NWQ == 4 && KSPLIT == 2 && QB == 1) {
+            if (p.zigzag == 2) {
+                // query waves 0-1 take 64-row tile n64 - 1 - rank, waves 2-3 tile rank
+                // (none when the two coincide); the key range covers both
+                const int n64 = (N + 63) >> 6;
+                const int heavy = n64 - 1 - rank, light = rank;
+                const bool upper = x.wave_q < NWQ / 2;
+                x.qw0 = upper ? heavy * 64 + x.wave_q * 32
+                              : (light < heavy ? light * 64 + (x.wave_q - NWQ / 2) * 32 : N);
+                row_lo = light * 64;
+                row_hi = min(heavy * 64 + 63, N - 1);
+            }
+        }
         pos_range(p, q_off, x.qw0, min(x.qw0 + QB * 32, N) - 1, x.pw0, x.w_last);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) x.lpos[qb] = pos_of(p, q_off, x.qw0 + qb * 32 + x.l32);
@@ -558,7 +582,7 @@ struct Kernel {
         // ---- key tiles seen by the workgroup (within its key split), divided
         // between the key groups
         int p_first, p_last;
-        pos_range(p, q_off, q_tile0, min(q_tile0 + BM, N) - 1, p_first, p_last);
+        pos_range(p, q_off, row_lo, row_hi, p_first, p_last);
         int kv_lo = 0, kv_hi = Nk - 1;
         if constexpr (MASK != MASK_NONE) kv_hi = min(kv_hi, p_last);
         if constexpr (MASK == MASK_WINDOW) kv_lo = max(0, p_first - p.window + 1);
@@ -567,13 +591,23 @@ struct Kernel {
         const int t_last = min(kv_hi / BN, s_first + p.split_tiles - 1);
         const int n_tiles = Nk > 0 ? max(0, t_last + 1 - t_begin) : 0;
         const int half = (n_tiles + KSPLIT - 1) / KSPLIT;
-        const int my_begin = t_begin + x.kgroup * half;
-        const int my_count = max(0, min(half, n_tiles - x.kgroup * half));
+        int my_begin = t_begin + x.kgroup * half;
+        int my_count = max(0, min(half, n_tiles - x.kgroup * half));
+        x.tstride = 1;
 
         // ---- two-term P for query tiles whose first row sees few keys
         int min_vis = Nk;
         if constexpr (MASK != MASK_NONE) min_vis = min(Nk, p_first + 1);
         if constexpr (MASK == MASK_WINDOW) min_vis = min(min_vis, p.window);
+        if constexpr (PAIRABLE) {
+            if (p.zigzag == 2) {
+                // alternate tiles per key group; the P mode follows the wave's own rows
+                my_begin = t_begin + x.kgroup;
+                my_count = max(0, (n_tiles - x.kgroup + 1) / 2);
+                x.tstride = 2;
+                min_vis = min(Nk, x.pw0 + 1);
+            }
+        }
         const bool exact = min_vis < p.exact_below;
 
         // ---- prologue: the first NSTAGE-1 tiles (two with PAIR) in flight, then the main
@@ -581,7 +615,7 @@ struct Kernel {
         x.loader = x.wave_q < NWQ / 2;
 #pragma unroll
         for (int s = 0; s < (PAIR ? 2 : NSTAGE - 1); ++s)
-            if (s < my_count) load_tile_step(x, my_begin + s, x.kst[s], x.vst[s]);
+            if (s < my_count) load_tile_step(x, tile_at(x, my_begin, s), x.kst[s], x.vst[s]);
         if (exact)
             loop<true>(x, st, half, my_begin, my_count);
         else

@@ -111,18 +111,21 @@ def test_launch_rejects_before_touching_the_gpu():
 def test_auto_config_choice():
     """The automatic tile configuration follows the documented rule: for d=64,
     32-row workgroups with four key groups when there are at most 256 of
-    them, else 64-row workgroups for masked runs and small grids and 128-row
-    workgroups for large unmasked grids; 256-row workgroups for large d=128
-    grids."""
+    them; else, causal, 128-row workgroups of paired 64-row tiles from 128
+    such workgroups up (64-row ones below), with a window 64-row workgroups
+    up to 512 128-row tiles, and unmasked 128-row workgroups unless the grid
+    is small; 256-row workgroups for large d=128 grids."""
     auto = lambda *a: fa.attn_fwd_plan_ex(*a, -1)["config_id"]
-    assert auto(2, 4, 4, 4096, 64, 1, 0, 0) == 2        # lab, causal
+    assert auto(2, 4, 4, 4096, 64, 1, 0, 0) == 0        # lab, causal: paired 64-row tiles
     assert auto(2, 4, 4, 4096, 64, 0, 0, 0) == 0        # lab, full
     assert auto(2, 4, 4, 1024, 64, 0, 0, 0) == 4        # small grid: 32 rows, four key groups
     assert auto(2, 4, 4, 1024, 64, 1, 0, 0) == 4
     assert auto(2, 4, 4, 256, 64, 1, 0, 0) == 4
-    assert auto(2, 4, 4, 2048, 64, 1, 0, 0) == 2        # 512 32-row workgroups
+    assert auto(2, 4, 4, 2048, 64, 1, 0, 0) == 0        # 512 32-row workgroups, 128 of 128 rows
+    assert auto(1, 6, 6, 2048, 64, 1, 0, 0) == 2        # 96 of 128 rows: 64-row workgroups
+    assert auto(2, 4, 4, 4096, 64, 1, 512, 0) == 2      # window
     assert auto(1, 12, 12, 2048, 64, 0, 0, 0) == 0      # stress, full
-    assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 2      # stress, causal
+    assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 0      # stress, causal
     assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 1      # GQA prefill
     assert auto(1, 32, 1, 32768, 128, 1, 4096, 1) == 1  # MQA with window
     assert auto(1, 2, 2, 512, 128, 1, 0, 1) == 0        # small d=128 grid
@@ -239,6 +242,10 @@ def test_paged_plan():
     assert fa.attn_fwd_paged_workspace_size(4, 32, 8, 1, 128, 16, 3000, 512, 8192, 1, 0, 1) == p["workspace_bytes"]
     w = fa.attn_fwd_paged_plan(1, 32, 1, 1, 128, 16, 3000, 2048, 32768, 1, 4096, 1)
     assert w["n_splits"] * w["split_tiles"] >= 32768 // w["block_n"]   # lengths vary: chunks span all keys
+    # causal prefill: the contiguous call pairs 64-row tiles in 128-row
+    # workgroups, the paged kernel does not pair them and keeps 64-row ones
+    assert fa.attn_fwd_splitkv_plan(2, 4, 4, 4096, 4096, 64, 1, 0, 0)["config_id"] == 0
+    assert fa.attn_fwd_paged_plan(2, 4, 4, 4096, 64, 16, 2048, 256, 4096, 1, 0, 0)["config_id"] == 2
 
 
 def test_autotune_rejects_before_touching_the_gpu():

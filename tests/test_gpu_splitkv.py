@@ -42,6 +42,10 @@ CASES = [
     (2, 8, 2, 17, 600, 128, "f16", True, 0),      # one row too many to stack
     (1, 2, 1, 300, 300, 128, "bf16", True, 0),    # square: the plain forward's function
     (1, 3, 3, 257, 257, 64, "f16", True, 64),
+    # several 64-row query tiles below a longer cache: the 128-row
+    # configuration pairs tiles r and n - 1 - r with a query offset
+    (1, 2, 2, 333, 2000, 64, "f16", True, 0),
+    (1, 4, 2, 200, 900, 128, "bf16", True, 0),
 ]
 
 
