@@ -52,6 +52,12 @@ const TileCfg &tile_cfg(int64_t d, int id) { return d == 64 ? kCfg64[id] : kCfg1
 // Query tiles whose first row sees fewer keys than this use the two-term P.
 constexpr int kExactBelow = 256;
 
+// Causal runs of the 128-row configuration pair 64-row query tiles r and
+// n - 1 - r per workgroup (equal work) while the grid fits one resident round;
+// on larger grids heavy-first dispatch balances the load and the paired
+// layout, whose light waves finish early, is slower.
+constexpr int64_t kPairMaxGrid = 256;
+
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxSplits = 1024;
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
@@ -92,10 +98,15 @@ int auto_config(int64_t B, int64_t Hq, int64_t N, int64_t d, int mask, bool pair
         return wg256 >= 512 ? 1 : 0;
     }
     if (B * Hq * ((N + 31) / 32) <= 256) return 4;
-    // causal: configuration 0 runs paired 64-row tiles of equal work (where the
-    // launch can pair them: not for paged K/V or stacked heads); below about one
-    // workgroup per compute unit the 64-row workgroups fill more units
-    if (mask == attnfwd::MASK_CAUSAL && pairs) return wg128 >= 128 ? 0 : 2;
+    // causal: below about one 128-row workgroup per compute unit the 64-row
+    // workgroups fill more units; up to one resident round configuration 0 with
+    // paired 64-row tiles of equal work (where the launch can pair them: not for
+    // paged K/V or stacked heads); on large grids the 256-row workgroups
+    if (mask == attnfwd::MASK_CAUSAL && pairs) {
+        if (wg128 < 128) return 2;
+        if (B * Hq * ((N + 255) / 256) >= 1024) return 1;
+        return 0;
+    }
     if (mask != attnfwd::MASK_NONE) return wg128 <= 512 ? 2 : 0;
     return wg128 < 128 ? 2 : 0;
 }
@@ -387,7 +398,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse
     // two 64-row workgroups share a compute unit: pair heavy and light tiles;
     // causal, 128 rows: two 64-row tiles of equal combined work per workgroup
     // (ceil(ceil(N / 64) / 2) = ceil(N / 128) pairs: the grid is the same)
-    p.zigzag = (id == 2) ? 1 : (id == 0 && mask == attnfwd::MASK_CAUSAL) ? 2 : 0;
+    p.zigzag = (id == 2) ? 1 : (id == 0 && mask == attnfwd::MASK_CAUSAL && grid <= kPairMaxGrid) ? 2 : 0;
     const hipError_t err = launch(d, dtype, mask, id, p, grid, (hipStream_t)stream);
     return status_of(err);
 }
@@ -489,7 +500,8 @@ int attn_fwd_splitkv_ex(const void *q, const void *k, const void *v, void *o, fl
                            scale, sp.ntiles);
     p.q_off = (int)(Nk - Nq);
     p.pack_nq = kv.pack_nq;
-    p.zigzag = (id == 2) ? 1 : (id == 0 && mask == attnfwd::MASK_CAUSAL && kv.pack_nq == 0) ? 2 : 0;
+    p.zigzag = (id == 2) ? 1
+               : (id == 0 && mask == attnfwd::MASK_CAUSAL && kv.pack_nq == 0 && sp.grid <= kPairMaxGrid) ? 2 : 0;
     p.n_splits = (int)sp.n_splits;
     p.split_tiles = (int)sp.split_tiles;
     p.split_t0 = (int)sp.t0;

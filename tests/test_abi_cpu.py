@@ -111,8 +111,9 @@ def test_launch_rejects_before_touching_the_gpu():
 def test_auto_config_choice():
     """The automatic tile configuration follows the documented rule: for d=64,
     32-row workgroups with four key groups when there are at most 256 of
-    them; else, causal, 128-row workgroups of paired 64-row tiles from 128
-    such workgroups up (64-row ones below), with a window 64-row workgroups
+    them; else, causal, 64-row workgroups under 128 128-row ones, 256-row
+    workgroups from 1024 of them, 128-row workgroups between (paired 64-row
+    tiles up to 256 workgroups), with a window 64-row workgroups
     up to 512 128-row tiles, and unmasked 128-row workgroups unless the grid
     is small; 256-row workgroups for large d=128 grids."""
     auto = lambda *a: fa.attn_fwd_plan_ex(*a, -1)["config_id"]
@@ -126,6 +127,8 @@ def test_auto_config_choice():
     assert auto(2, 4, 4, 4096, 64, 1, 512, 0) == 2      # window
     assert auto(1, 12, 12, 2048, 64, 0, 0, 0) == 0      # stress, full
     assert auto(1, 12, 12, 2048, 64, 1, 0, 0) == 0      # stress, causal
+    assert auto(1, 4, 4, 16384, 64, 1, 0, 0) == 0       # 256 256-row workgroups
+    assert auto(4, 16, 16, 4096, 64, 1, 0, 0) == 1      # 1024 256-row workgroups
     assert auto(4, 32, 8, 8192, 128, 1, 0, 1) == 1      # GQA prefill
     assert auto(1, 32, 1, 32768, 128, 1, 4096, 1) == 1  # MQA with window
     assert auto(1, 2, 2, 512, 128, 1, 0, 1) == 0        # small d=128 grid

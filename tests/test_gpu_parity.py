@@ -304,3 +304,15 @@ def test_softmax_stress_patterns(fa, pattern, d, dtype):
             ro, rl = oracle_full(q, k, v, causal=causal)
             o, lse = run_gpu(q, k, v, causal=causal, config_id=cfg)
             check(f"softmax stress {pattern} d{d} {dtype} causal={causal} cfg{cfg}", o, lse, ro, rl, dtype)
+
+
+def test_causal_128_row_layouts(fa):
+    """Configuration 0, causal: paired 64-row query tiles on grids of at most
+    256 workgroups, heavy-first 128-row tiles above (B=2, 65 and 64 heads of
+    N=640: 650 and 640 workgroups; B=1, 2 heads: 10)."""
+    for B, Hq, N, dt in ((2, 65, 640, "f16"), (2, 64, 640, "bf16"), (1, 2, 640, "bf16")):
+        plan = fa.attn_fwd_plan_ex(B, Hq, Hq, N, 64, 1, 0, 0 if dt == "f16" else 1, 0)
+        q, k, v = inputs(B, Hq, Hq, N, 64, dt, seed=B * 1000 + Hq)
+        ro, rl = oracle_full(q, k, v, causal=True, window=0)
+        o, lse = run_gpu(q, k, v, causal=True, window=0, config_id=0)
+        check(f"B{B} Hq{Hq} N{N} {dt} grid {plan['grid']}", o, lse, ro, rl, dt)
